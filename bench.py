@@ -1,0 +1,251 @@
+#!/usr/bin/env python3
+"""Benchmark: one rank's lap of ring attention on one MI355X.
+
+A step is one whole lap: the empty state, P block steps (each block after the
+rank's own arrives through an emulated ring transfer on a side stream), and the
+finalize pass, on seeded synthetic bf16 inputs already resident in HBM.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--rank R]
+
+Prints ONE JSON line.  ``value`` is useful attention TFLOP/s: 4 * head_dim flops
+per allowed (query, key) pair per query head, over the timed laps.  The
+``roofline`` object prices the step kernel alone (its flops per launch over its
+average launch time, from HIP events recorded around each launch on the compute
+stream) against the MI355X dense bf16 MFMA peak; ``cpu_baseline`` times the
+fp64 oracle on this host's cores over a bounded sample of the same workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6   # 256 CU x 2.4 GHz x 4096 dense bf16 flop/clk/CU (MI355X)
+PEAK_HBM_GBS = 8000.0
+DEFAULT_WORKLOAD = "noncausal_n131072_p8_h32"
+MASK_CODE = {"none": 0, "causal_contiguous": 1, "causal_striped": 2}
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "step_bf16_traffic.txt")
+STEP_SOURCE = os.path.join(ROOT, "exact_long_context_amd", "csrc", "ra_step_bf16.hip")
+
+
+def log(msg: str) -> None:
+    print(msg, file=sys.stderr, flush=True)
+
+
+def kernel_source_sha() -> str:
+    return hashlib.sha256(open(STEP_SOURCE, "rb").read()).hexdigest()[:16]
+
+
+def read_traffic(workload: str):
+    """HBM bytes per step-kernel launch from the committed rocprofv3 counter summary,
+    or None if it is missing, for another workload, or older than the kernel source."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    kv = {}
+    for ln in open(TRAFFIC_FILE):
+        if ":" in ln and not ln.startswith("#"):
+            k, v = ln.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("kernel_source_sha") != kernel_source_sha() or kv.get("workload") != workload:
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(w, rank: int, q, k, v, seconds: float):
+    """Time the fp64 oracle on this host over whole row chunks of one head (all keys)."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    causal = w.mask != "none"
+    q_pos = oracle.tokens_of_rank(w.N, w.P, w.layout, rank)
+    k_pos = np.arange(w.N)
+    g = 0
+    q64 = q[0, 0:1].double().numpy()[None]
+    k64 = k[0, g:g + 1].double().numpy()[None]
+    v64 = v[0, g:g + 1].double().numpy()[None]
+    chunk = 256 if w.N <= 262144 else 32    # keeps the fp64 score chunk near 256 MiB
+    done_rows = 0
+    flops = 0
+    t0 = time.perf_counter()
+    while done_rows < w.n_local and time.perf_counter() - t0 < seconds:
+        rows = np.arange(done_rows, min(done_rows + chunk, w.n_local))
+        oracle.dense_attention(q64, k64, v64, q_pos, k_pos, causal, rows=rows, row_chunk=chunk)
+        pairs = oracle.live_pair_count(q_pos[rows], k_pos, causal)
+        flops += 4 * w.head_dim * pairs
+        done_rows += rows.size
+    el = time.perf_counter() - t0
+    return {
+        "value": flops / el / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": (f"fp64 dense attention (oracle.dense_attention) of head 0, local rows 0..{done_rows - 1} "
+                   f"of rank {rank} against all {w.N} keys, {el:.1f} s; same useful-flop accounting"),
+        "seconds": round(el, 3),
+    }
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10, help="timed laps")
+    ap.add_argument("--warmup", type=int, default=3, help="untimed laps")
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--rank", type=int, default=None, help="measured rank (default: the workload's first)")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="oracle timing budget")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs one rank's lap on one GPU; --gpus {args.gpus} is not supported "
+              "(the ring is emulated on a single device and nothing here spans GPUs)", file=sys.stderr)
+        return 2
+
+    import torch
+    import synth
+    import exact_long_context_amd as ra
+    from exact_long_context_amd.workload import shard_blocks, useful_flops
+
+    if not torch.cuda.is_available():
+        print("bench.py needs an MI355X GPU", file=sys.stderr)
+        return 2
+    w = synth.WORKLOADS[args.workload]
+    rank = w.ranks[0] if args.rank is None else args.rank
+    mask = MASK_CODE[w.mask]
+    dev = torch.device("cuda", 0)
+
+    log(f"[bench] generating {w.name} rank {rank}")
+    t0 = time.perf_counter()
+    q, k, v = synth.workload_tensors(w, rank)
+    if w.global_q:   # the tiny workload draws Q globally: keep this rank's rows
+        n = w.n_local
+        q = q[:, :, rank * n:(rank + 1) * n] if w.layout == "contiguous" else q[:, :, rank::w.P]
+        q = q.contiguous()
+    qd = q.to(dev)
+    kd, vd = k.to(dev), v.to(dev)
+    kb, vb = shard_blocks(kd, vd, w.P, w.layout)
+    del kd, vd
+    torch.cuda.synchronize()
+    log(f"[bench] inputs ready in {time.perf_counter() - t0:.1f} s")
+
+    ring = ra.EmulatedRing(kb, vb)
+    desc = ra.desc_for(qd, kb[0], w.P)
+    ws = torch.empty(ra.workspace_bytes(desc), dtype=torch.uint8, device=dev)
+    out = torch.empty((w.batch, w.q_heads, w.n_local, w.head_dim), dtype=torch.float32, device=dev)
+    lse = torch.empty((w.batch, w.q_heads, w.n_local), dtype=torch.float32, device=dev)
+
+    # per-step work from the host planner (the same decisions the kernels take)
+    order = [((rank - s) % w.P + w.P) % w.P for s in range(w.P)]
+    step_flops = []
+    for j in order:
+        qo, ko = ra.block_offsets(mask, rank, j, w.n_local, w.n_local)
+        step_flops.append(useful_flops(ra.plan_block(desc, w.n_local, mask, qo, ko)["live_pairs"], w.head_dim))
+    lap_flops = sum(step_flops)
+
+    def mk_events():
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(2 * w.P)]
+        for e in evs:
+            e.record()
+        return evs
+
+    for i in range(args.warmup):
+        ring.lap(qd, rank, mask, workspace=ws, out=out, lse=lse)
+    events = [mk_events() for _ in range(args.steps)]
+    torch.cuda.synchronize()
+
+    t_start = time.perf_counter()
+    stats = None
+    for i in range(args.steps):
+        _, _, stats = ring.lap(qd, rank, mask, workspace=ws, out=out, lse=lse, step_events=events[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t_start
+    ms_per_lap = 1000.0 * elapsed / args.steps
+    value = lap_flops * args.steps / elapsed / 1e12
+    assert stats["live_pairs"] * 4 * w.head_dim == lap_flops
+
+    # step-kernel launch times from the events (steps that launched a kernel only)
+    per_step_ms = [[evs[2 * s].elapsed_time(evs[2 * s + 1]) for s in range(w.P)] for evs in events]
+    # end of step s-1 to start of step s: launch gap plus any wait for the block's transfer
+    gaps_ms = [[evs[2 * s - 1].elapsed_time(evs[2 * s]) for s in range(1, w.P)] for evs in events]
+    live_steps = [s for s in range(w.P) if step_flops[s] > 0]
+    kern_ms = sum(per_step_ms[i][s] for i in range(args.steps) for s in live_steps)
+    kern_launches = len(live_steps) * args.steps
+    achieved = sum(step_flops) * args.steps / (kern_ms / 1000.0) / 1e12 if kern_ms > 0 else 0.0
+    avg_kernel_ms = kern_ms / max(kern_launches, 1)
+
+    traffic = read_traffic(w.name)
+    roofline = {
+        "bound": "mfma",
+        "achieved": round(achieved, 2),
+        "peak": PEAK_BF16_TFLOPS,
+        "unit": "TFLOP/s",
+        "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+        "traffic": traffic,
+        "kernel": "step_bf16_kernel<128>",
+        "flops_per_launch": step_flops[live_steps[0]] if live_steps else 0,
+        "avg_launch_ms": round(avg_kernel_ms, 4),
+    }
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] timing the oracle on host cores")
+        cpu = cpu_baseline(w, rank, q, k, v, args.cpu_seconds)
+
+    props = torch.cuda.get_device_properties(0)
+    line = {
+        "metric": "useful attention TFLOP/s per GPU (one rank's lap) and % of bf16 MFMA peak",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_lap, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded i.i.d. Gaussian Q/K/V, see synth/)",
+        "config": {
+            "workload": w.name, "N": w.N, "P": w.P, "rank": rank, "batch": w.batch,
+            "q_heads": w.q_heads, "kv_heads": w.kv_heads, "head_dim": w.head_dim,
+            "q_len": w.n_local, "kv_block": w.n_local, "mask": w.mask, "layout": w.layout,
+            "value_scale": w.value_scale,
+        },
+        "pct_of_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "detail": {
+            "useful_flops_per_lap": lap_flops,
+            "live_pairs_per_lap": stats["live_pairs"],
+            "blocks_run": stats["blocks_run"], "blocks_skipped": stats["blocks_skipped"],
+            "tiles": {"full": stats["tiles_full"], "partial": stats["tiles_partial"],
+                      "empty": stats["tiles_empty"], "tile_q": stats["tile_q"], "tile_k": stats["tile_k"]},
+            "step_kernel_ms_median": [round(sorted(col)[len(col) // 2], 4) for col in zip(*per_step_ms)],
+            "gap_before_step_ms_median": [round(sorted(col)[len(col) // 2], 4) for col in zip(*gaps_ms)],
+            "peak_mem_gib": round(torch.cuda.max_memory_allocated() / 2**30, 2),
+            "gpu": props.name, "cus": props.multi_processor_count,
+            "torch": torch.__version__, "hip": torch.version.hip,
+            "kernel_source_sha": kernel_source_sha(),
+        },
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

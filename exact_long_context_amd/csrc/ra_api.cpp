@@ -1,0 +1,350 @@
+// ra_api.cpp -- the C ABI (include/ra.h): argument validation, the block/tile planner
+// and the launches of the step and finalize kernels.
+//
+// The planner is host-only arithmetic on the shared position algebra (ra_pos.h), so the
+// same decisions the kernels take can be inspected without a GPU (ra_plan_block,
+// ra_tile_classes).
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <new>
+
+#include "../../include/ra.h"
+#include "ra_internal.h"
+#include "ra_pos.h"
+
+struct ra_state {
+  ra_desc desc;
+  const void* q;
+  float* o_acc;
+  float* m;
+  float* l;
+  int fresh;       // no step has written the workspace yet
+  int finalized;
+  ra_stats stats;
+  unsigned long long* dbg;
+};
+
+namespace {
+
+thread_local char g_err[256] = "";
+
+int fail(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(RA_E_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+int elem_bytes(int32_t dtype) { return dtype == RA_DTYPE_BF16 ? 2 : 4; }
+
+int tile_q_of(const ra_desc* d) { return d->dtype == RA_DTYPE_BF16 ? ra::kBf16TileQ : ra::kF32TileQ; }
+int tile_k_of(const ra_desc* d) { return d->dtype == RA_DTYPE_BF16 ? ra::kBf16TileK : ra::kF32TileK; }
+
+// Checks a descriptor; the pointer checks are separate.
+int check_desc(const ra_desc* d) {
+  if (!d) return fail(RA_E_INVALID, "desc is NULL");
+  if (d->batch < 1 || d->q_heads < 1 || d->kv_heads < 1)
+    return fail(RA_E_INVALID, "batch, q_heads and kv_heads must be >= 1");
+  if (d->q_heads % d->kv_heads)
+    return fail(RA_E_INVALID, "q_heads (%d) is not a multiple of kv_heads (%d)", d->q_heads, d->kv_heads);
+  if (d->q_len < 0) return fail(RA_E_INVALID, "q_len must be >= 0");
+  if (d->ring_size < 1) return fail(RA_E_INVALID, "ring_size must be >= 1");
+  if (d->dtype != RA_DTYPE_BF16 && d->dtype != RA_DTYPE_F32)
+    return fail(RA_E_UNSUPPORTED, "dtype %d is not supported", d->dtype);
+  if (d->head_dim != 64 && d->head_dim != 128)
+    return fail(RA_E_UNSUPPORTED, "head_dim %d is not supported (64 or 128)", d->head_dim);
+  if (!(std::isfinite(d->softmax_scale) && d->softmax_scale >= 0.f))
+    return fail(RA_E_INVALID, "softmax_scale must be finite and >= 0 (0 selects 1/sqrt(d))");
+  // vector loads need 16-byte aligned rows
+  const int64_t vec = 16 / elem_bytes(d->dtype);
+  for (int i = 0; i < 3; ++i) {
+    if (d->q_strides[i] < 0 || d->kv_strides[i] < 0)
+      return fail(RA_E_INVALID, "strides must be >= 0");
+    if (d->q_strides[i] % vec || d->kv_strides[i] % vec)
+      return fail(RA_E_INVALID, "strides must be multiples of %lld elements (16-byte rows)",
+                  (long long)vec);
+  }
+  if (d->q_len > 1 && d->q_strides[2] < d->head_dim)
+    return fail(RA_E_INVALID, "q token stride smaller than head_dim");
+  return RA_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+struct Layout {
+  size_t o_off, m_off, l_off, total;
+};
+
+Layout layout_of(const ra_desc* d) {
+  const size_t rows = (size_t)d->batch * d->q_heads * d->q_len;
+  Layout L;
+  L.o_off = 0;
+  L.m_off = align256(rows * d->head_dim * sizeof(float));
+  L.l_off = L.m_off + align256(rows * sizeof(float));
+  L.total = rows ? L.l_off + align256(rows * sizeof(float)) : 0;
+  return L;
+}
+
+int32_t pos_stride(int32_t mask_kind, const ra_desc* d) {
+  return mask_kind == RA_MASK_CAUSAL_STRIPED ? d->ring_size : 1;
+}
+
+// Plan one block: counts for the whole launch (all batches and query heads).
+int plan(const ra_desc* d, int32_t kv_len, int32_t mask_kind, int64_t q_off, int64_t k_off,
+         ra_stats* out, int32_t* diag_out) {
+  if (kv_len < 0) return fail(RA_E_INVALID, "kv_len must be >= 0");
+  if (mask_kind < RA_MASK_NONE || mask_kind > RA_MASK_CAUSAL_STRIPED)
+    return fail(RA_E_INVALID, "unknown mask_kind %d", mask_kind);
+  const int causal = mask_kind != RA_MASK_NONE;
+  const int32_t s = pos_stride(mask_kind, d);
+  const int32_t diag = ra::diag_shift(causal, q_off, k_off, s, d->q_len, kv_len);
+  const int tq = tile_q_of(d), tk = tile_k_of(d);
+  std::memset(out, 0, sizeof *out);
+  out->tile_q = tq;
+  out->tile_k = tk;
+  const int64_t heads = (int64_t)d->batch * d->q_heads;
+  int64_t pairs = 0;
+  for (int32_t i = 0; i < d->q_len; ++i) pairs += ra::keys_visible(i, diag, kv_len);
+  int64_t full = 0, live = 0;
+  const int32_t n_qt = (d->q_len + tq - 1) / tq;
+  const int32_t n_kt = (kv_len + tk - 1) / tk;
+  for (int32_t a = 0; a < n_qt; ++a) {
+    const int32_t i0 = a * tq, i1 = i0 + tq < d->q_len ? i0 + tq : d->q_len;
+    full += ra::tiles_full(i0, i1, diag, kv_len, tk);
+    live += ra::tiles_live(i0, i1, diag, kv_len, tk);
+  }
+  out->live_pairs = pairs * heads;
+  out->tiles_full = full * heads;
+  out->tiles_partial = (live - full) * heads;
+  out->tiles_empty = ((int64_t)n_qt * n_kt - live) * heads;
+  if (pairs > 0) out->blocks_run = 1; else out->blocks_skipped = 1;
+  if (diag_out) *diag_out = diag;
+  return RA_OK;
+}
+
+void add_stats(ra_stats* acc, const ra_stats* s) {
+  acc->live_pairs += s->live_pairs;
+  acc->tiles_full += s->tiles_full;
+  acc->tiles_partial += s->tiles_partial;
+  acc->tiles_empty += s->tiles_empty;
+  acc->blocks_run += s->blocks_run;
+  acc->blocks_skipped += s->blocks_skipped;
+  acc->tile_q = s->tile_q;
+  acc->tile_k = s->tile_k;
+}
+
+int make_state(const ra_desc* d, const void* q, void* ws, int fresh, ra_state** out) {
+  if (!out) return fail(RA_E_INVALID, "out is NULL");
+  *out = nullptr;
+  int rc = check_desc(d);
+  if (rc) return rc;
+  const Layout L = layout_of(d);
+  if (d->q_len > 0) {
+    if (!q) return fail(RA_E_INVALID, "Q_r is NULL");
+    if (!ws) return fail(RA_E_INVALID, "workspace is NULL");
+    if (!aligned16(q)) return fail(RA_E_INVALID, "Q_r must be 16-byte aligned");
+    if ((reinterpret_cast<uintptr_t>(ws) & 255) != 0)
+      return fail(RA_E_INVALID, "workspace must be 256-byte aligned");
+  }
+  ra_state* st = new (std::nothrow) ra_state;
+  if (!st) return fail(RA_E_INVALID, "out of host memory");
+  std::memset(st, 0, sizeof *st);
+  st->desc = *d;
+  if (st->desc.softmax_scale == 0.f) st->desc.softmax_scale = 1.0f / std::sqrt((float)d->head_dim);
+  st->q = q;
+  char* base = static_cast<char*>(ws);
+  st->o_acc = reinterpret_cast<float*>(base + L.o_off);
+  st->m = reinterpret_cast<float*>(base + L.m_off);
+  st->l = reinterpret_cast<float*>(base + L.l_off);
+  st->fresh = fresh;
+  st->stats.tile_q = tile_q_of(d);
+  st->stats.tile_k = tile_k_of(d);
+  *out = st;
+  return RA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t ra_workspace_bytes(const ra_desc* desc) {
+  if (check_desc(desc)) return 0;
+  return layout_of(desc).total;
+}
+
+int ra_workspace_layout(const ra_desc* desc, size_t* o_off, size_t* m_off, size_t* l_off) {
+  int rc = check_desc(desc);
+  if (rc) return rc;
+  const Layout L = layout_of(desc);
+  if (o_off) *o_off = L.o_off;
+  if (m_off) *m_off = L.m_off;
+  if (l_off) *l_off = L.l_off;
+  return RA_OK;
+}
+
+int ra_state_init(const ra_desc* desc, const void* q, void* workspace, ra_state** out) {
+  return make_state(desc, q, workspace, 1, out);
+}
+
+int ra_state_resume(const ra_desc* desc, const void* q, void* workspace, ra_state** out) {
+  return make_state(desc, q, workspace, 0, out);
+}
+
+int ra_block_step(ra_state* st, const void* k, const void* v, int32_t kv_len, int32_t mask_kind,
+                  int64_t q_offset, int64_t k_offset) {
+  if (!st) return fail(RA_E_INVALID, "state is NULL");
+  if (st->finalized) return fail(RA_E_STATE, "step after finalize");
+  const ra_desc* d = &st->desc;
+  ra_stats s;
+  int32_t diag = 0;
+  int rc = plan(d, kv_len, mask_kind, q_offset, k_offset, &s, &diag);
+  if (rc) return rc;
+  if (kv_len > 0) {
+    if (!k || !v) return fail(RA_E_INVALID, "K_j or V_j is NULL");
+    if (!aligned16(k) || !aligned16(v)) return fail(RA_E_INVALID, "K_j and V_j must be 16-byte aligned");
+    if (kv_len > 1 && d->kv_strides[2] < d->head_dim)
+      return fail(RA_E_INVALID, "kv token stride smaller than head_dim");
+  }
+  if (s.blocks_run == 0) {  // no allowed pair in the whole block: nothing to do
+    add_stats(&st->stats, &s);
+    return RA_OK;
+  }
+  ra::StepParams p;
+  p.q = st->q;
+  p.k = k;
+  p.v = v;
+  p.o_acc = st->o_acc;
+  p.m = st->m;
+  p.l = st->l;
+  p.q_sb = d->q_strides[0];
+  p.q_sh = d->q_strides[1];
+  p.q_st = d->q_strides[2];
+  p.k_sb = d->kv_strides[0];
+  p.k_sh = d->kv_strides[1];
+  p.k_st = d->kv_strides[2];
+  p.batch = d->batch;
+  p.q_heads = d->q_heads;
+  p.kv_heads = d->kv_heads;
+  p.group = d->q_heads / d->kv_heads;
+  p.n_q = d->q_len;
+  p.n_k = kv_len;
+  p.diag = diag;
+  p.scale_log2 = d->softmax_scale * 1.4426950408889634f;
+  p.fresh = st->fresh;
+  p.dbg = st->dbg;
+  hipStream_t stream = static_cast<hipStream_t>(d->stream);
+  hipError_t e = d->dtype == RA_DTYPE_BF16 ? ra::launch_step_bf16(p, d->head_dim, stream)
+                                           : ra::launch_step_f32(p, d->head_dim, stream);
+  if (e != hipSuccess) return hip_fail(e, "step kernel launch");
+  st->fresh = 0;
+  add_stats(&st->stats, &s);
+  return RA_OK;
+}
+
+int ra_finalize(ra_state* st, float* o, float* lse) {
+  if (!st) return fail(RA_E_INVALID, "state is NULL");
+  if (st->finalized) return fail(RA_E_STATE, "state already finalized");
+  const ra_desc* d = &st->desc;
+  const int64_t rows = (int64_t)d->batch * d->q_heads * d->q_len;
+  if (rows > 0 && !o) return fail(RA_E_INVALID, "O_r is NULL");
+  if (rows > 0 && !aligned16(o)) return fail(RA_E_INVALID, "O_r must be 16-byte aligned");
+  ra::FinalizeParams p;
+  p.o_acc = st->o_acc;
+  p.m = st->m;
+  p.l = st->l;
+  p.o = o;
+  p.lse = lse;
+  p.rows = rows;
+  p.d = d->head_dim;
+  p.fresh = st->fresh;
+  hipError_t e = ra::launch_finalize(p, static_cast<hipStream_t>(d->stream));
+  if (e != hipSuccess) return hip_fail(e, "finalize kernel launch");
+  st->finalized = 1;
+  return RA_OK;
+}
+
+int ra_state_destroy(ra_state* st) {
+  delete st;
+  return RA_OK;
+}
+
+int ra_get_stats(const ra_state* st, ra_stats* out) {
+  if (!st || !out) return fail(RA_E_INVALID, "state or out is NULL");
+  *out = st->stats;
+  return RA_OK;
+}
+
+int ra_state_set_debug_counters(ra_state* st, uint64_t* counters) {
+  if (!st) return fail(RA_E_INVALID, "state is NULL");
+  st->dbg = reinterpret_cast<unsigned long long*>(counters);
+  return RA_OK;
+}
+
+int ra_plan_block(const ra_desc* desc, int32_t kv_len, int32_t mask_kind, int64_t q_offset,
+                  int64_t k_offset, ra_stats* out) {
+  int rc = check_desc(desc);
+  if (rc) return rc;
+  if (!out) return fail(RA_E_INVALID, "out is NULL");
+  return plan(desc, kv_len, mask_kind, q_offset, k_offset, out, nullptr);
+}
+
+int ra_tile_classes(const ra_desc* desc, int32_t kv_len, int32_t mask_kind, int64_t q_offset,
+                    int64_t k_offset, uint8_t* host_out, size_t cap) {
+  int rc = check_desc(desc);
+  if (rc) return rc;
+  ra_stats s;
+  int32_t diag = 0;
+  rc = plan(desc, kv_len, mask_kind, q_offset, k_offset, &s, &diag);
+  if (rc) return rc;
+  const int tq = tile_q_of(desc), tk = tile_k_of(desc);
+  const int32_t n_qt = (desc->q_len + tq - 1) / tq;
+  const int32_t n_kt = (kv_len + tk - 1) / tk;
+  if ((size_t)n_qt * n_kt > cap) return fail(RA_E_INVALID, "host_out holds %zu bytes, need %lld", cap,
+                                             (long long)n_qt * n_kt);
+  if (n_qt * (int64_t)n_kt > 0 && !host_out) return fail(RA_E_INVALID, "host_out is NULL");
+  for (int32_t a = 0; a < n_qt; ++a) {
+    const int32_t i0 = a * tq, i1 = i0 + tq < desc->q_len ? i0 + tq : desc->q_len;
+    for (int32_t c = 0; c < n_kt; ++c) {
+      const int32_t t0 = c * tk, t1 = t0 + tk < kv_len ? t0 + tk : kv_len;
+      host_out[(size_t)a * n_kt + c] = (uint8_t)ra::classify_tile(i0, i1, t0, t1, diag);
+    }
+  }
+  return RA_OK;
+}
+
+const char* ra_status_string(int status) {
+  switch (status) {
+    case RA_OK: return "ok";
+    case RA_E_INVALID: return g_err[0] ? g_err : "invalid argument";
+    case RA_E_UNSUPPORTED: return g_err[0] ? g_err : "unsupported";
+    case RA_E_STATE: return g_err[0] ? g_err : "bad state";
+    case RA_E_HIP: return g_err[0] ? g_err : "HIP error";
+    default: return "unknown status";
+  }
+}
+
+int ra_version(void) { return 1; }
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------------------
+// internal helpers exported to the ring driver
+// ---------------------------------------------------------------------------------------
+namespace ra {
+int set_error(int code, const char* msg) { return fail(code, "%s", msg); }
+int set_hip_error(hipError_t e, const char* what) { return hip_fail(e, what); }
+}  // namespace ra

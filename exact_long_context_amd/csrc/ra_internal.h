@@ -1,0 +1,49 @@
+// ra_internal.h -- parameters shared by the C-ABI layer and the kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ra {
+
+// Everything one step launch needs.  Strides are in elements; the head dimension is
+// contiguous.  All position logic is already folded into `diag` (see ra_pos.h).
+struct StepParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  float* o_acc;        // O~ [B, Hq, n_q, D]
+  float* m;            // [B, Hq, n_q], base-2 units
+  float* l;            // [B, Hq, n_q]
+  int64_t q_sb, q_sh, q_st;
+  int64_t k_sb, k_sh, k_st;
+  int32_t batch, q_heads, kv_heads, group;  // group = q_heads / kv_heads
+  int32_t n_q, n_k;
+  int32_t diag;        // key t is visible to row i iff t <= i + diag
+  float scale_log2;    // softmax scale * log2(e)
+  int32_t fresh;       // 1: the state has never been written; start from the empty state
+  unsigned long long* dbg;  // optional device counters [3] (unmasked tiles, masked tiles, pairs)
+};
+
+struct FinalizeParams {
+  const float* o_acc;
+  const float* m;
+  const float* l;
+  float* o;
+  float* lse;          // may be null
+  int64_t rows;        // B * Hq * n_q
+  int32_t d;
+  int32_t fresh;       // 1: no step ever ran; write the empty result without reading
+};
+
+// Tile sizes of each kernel (the planner reports and classifies with these).
+constexpr int kBf16TileQ = 128;
+constexpr int kBf16TileK = 64;
+constexpr int kF32TileQ = 64;
+constexpr int kF32TileK = 32;
+
+hipError_t launch_step_bf16(const StepParams& p, int head_dim, hipStream_t stream);
+hipError_t launch_step_f32(const StepParams& p, int head_dim, hipStream_t stream);
+hipError_t launch_finalize(const FinalizeParams& p, hipStream_t stream);
+
+}  // namespace ra

@@ -1,0 +1,34 @@
+"""Device-side data placement for the emulated ring (torch plumbing only).
+
+Cuts global K/V [B, Hkv, N, d] into the P per-rank blocks a ring would hold:
+contiguous slices (rank j owns tokens j*N/P .. (j+1)*N/P - 1) or the striped
+round-robin layout (rank j owns tokens t with t mod P == j), each block made
+contiguous [B, Hkv, N/P, d] so it can be moved with one copy.  The positions of
+those tokens are not materialised: the library derives them from the block
+index (include/ra.h).
+"""
+
+from __future__ import annotations
+
+
+def shard_blocks(k_global, v_global, P: int, layout: str):
+    N = k_global.shape[2]
+    if N % P:
+        raise ValueError("N must be a multiple of P")
+    n = N // P
+    ks, vs = [], []
+    for j in range(P):
+        if layout == "contiguous":
+            ks.append(k_global[:, :, j * n:(j + 1) * n].contiguous())
+            vs.append(v_global[:, :, j * n:(j + 1) * n].contiguous())
+        elif layout == "striped":
+            ks.append(k_global[:, :, j::P].contiguous())
+            vs.append(v_global[:, :, j::P].contiguous())
+        else:
+            raise ValueError(layout)
+    return ks, vs
+
+
+def useful_flops(live_pairs: int, head_dim: int) -> int:
+    """4*d flops per allowed (query, key) pair per query head: 2d for the score, 2d for PV."""
+    return 4 * head_dim * live_pairs

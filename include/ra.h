@@ -1,0 +1,221 @@
+/*
+ * ra.h -- C ABI of librocring: one rank's lap of ring attention on one MI355X (gfx950).
+ *
+ * The operation, as the pages state it ("Ring Attention：把超长序列沿设备环流动",
+ * charlestar.github.io, section 环是怎样工作的, the forward loop):
+ *
+ *     state = empty online-softmax state for the local queries Q_r    -> ra_state_init
+ *     for each of the P KV blocks of the lap:
+ *         partial attention of Q_r against the block, merged into     -> ra_block_step
+ *         the state by the online-softmax rescale
+ *     local output = finalize(state)                                  -> ra_finalize
+ *
+ * The per-row state is the running maximum m, the running exponential sum l and the
+ * unnormalised output O~ ("GPU ring attention", aicassindra.com, section "Why partial
+ * results are allowed to merge"): when a block arrives both accumulators are rescaled by
+ * exp(old max - new max) and the block's contribution is added; after the lap
+ * O = O~ / l is exact softmax(scale * Q K^T) V over every allowed key.
+ *
+ * Masks are on global token positions.  Local query row i of this rank sits at global
+ * position  q_offset + i * s  and key t of the arriving block at  k_offset + t * s,
+ * where s = 1 for RA_MASK_NONE and RA_MASK_CAUSAL_CONTIGUOUS and s = ring_size for
+ * RA_MASK_CAUSAL_STRIPED (token t lives on rank t mod P).  The causal rule is: query
+ * position q may see key position k iff k <= q (same page, section Causal Attention
+ * 让环不再完全对称; positions are global, section 位置编码必须使用全局位置).  For a contiguous
+ * layout rank r passes q_offset = r * q_len and block j k_offset = j * kv_len; for the
+ * striped layout q_offset = r and k_offset = j.  Offsets are ignored for RA_MASK_NONE.
+ *
+ * Fully masked work is skipped at two granularities ("GPU ring attention", section
+ * "Striping the sequence to flatten the triangle"; charlestar page, Causal section,
+ * strictly-future / diagonal-crossing / unmasked rule): a block with no allowed pair
+ * launches nothing, and inside a launch a (query tile, key tile) with no allowed pair is
+ * never loaded or computed; only tiles that cross the diagonal apply the element mask.
+ *
+ * Conventions for every entry point
+ *  - Tensors are row-major with the head dimension contiguous.  Q_r is addressed as
+ *    Q[b*qs0 + h*qs1 + i*qs2 + c] (strides in elements, desc.q_strides), K_j and V_j as
+ *    K[b*ks0 + g*ks1 + t*ks2 + c] (desc.kv_strides, shared by K and V).  Query head h
+ *    reads KV head g = h / (q_heads / kv_heads) (contiguous GQA groups).
+ *  - All device pointers are caller-owned device memory (e.g. allocated by torch);
+ *    the library never allocates or frees device memory.  Host pointers are marked.
+ *  - All device work is enqueued asynchronously on desc.stream (a hipStream_t; NULL is
+ *    the null stream).  Device faults surface at the caller's next synchronisation.
+ *  - Return value: RA_OK (0) or a negative RA_E_* code; nothing is enqueued on error.
+ *    No C++ exception crosses the ABI.  ra_status_string() gives the text, including
+ *    the HIP error for RA_E_HIP (kept per host thread).
+ *  - One ra_state is driven by one host thread and one stream at a time.
+ */
+#ifndef RA_H_
+#define RA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ---------------------------------------------------------------- */
+#define RA_OK 0
+#define RA_E_INVALID (-1)     /* null pointer, bad dimension, q_heads % kv_heads != 0, bad stride or alignment */
+#define RA_E_UNSUPPORTED (-2) /* head_dim or dtype this build has no kernel for */
+#define RA_E_STATE (-3)       /* step or finalize on a finalized state, double finalize */
+#define RA_E_HIP (-4)         /* a HIP runtime call or kernel launch failed */
+
+/* ---- enums ----------------------------------------------------------------------- */
+typedef enum {
+  RA_MASK_NONE = 0,               /* every key of every block is allowed */
+  RA_MASK_CAUSAL_CONTIGUOUS = 1,  /* k <= q, positions offset + index (stride 1) */
+  RA_MASK_CAUSAL_STRIPED = 2      /* k <= q, positions offset + index * ring_size */
+} ra_mask_kind;
+
+typedef enum {
+  RA_DTYPE_BF16 = 0,  /* Q, K, V in bfloat16; MFMA with fp32 accumulation */
+  RA_DTYPE_F32 = 1    /* Q, K, V in float32; all arithmetic in fp32 (exactness path) */
+} ra_dtype;
+
+/* Tile classes reported by ra_tile_classes (same values as the oracle's enumeration). */
+#define RA_TILE_EMPTY 0
+#define RA_TILE_FULL 1
+#define RA_TILE_PARTIAL 2
+
+/* ---- descriptors ----------------------------------------------------------------- */
+typedef struct ra_desc {
+  int32_t batch;          /* B >= 1 */
+  int32_t q_heads;        /* Hq >= 1 */
+  int32_t kv_heads;       /* Hkv >= 1, Hq % Hkv == 0 */
+  int32_t q_len;          /* local query rows n >= 0 (any length; a ragged tail is fine) */
+  int32_t head_dim;       /* d: 64 or 128 */
+  int32_t dtype;          /* ra_dtype of Q, K and V; the state is always fp32 */
+  float softmax_scale;    /* 0 selects 1/sqrt(head_dim) */
+  int32_t ring_size;      /* P >= 1: position stride of RA_MASK_CAUSAL_STRIPED */
+  int64_t q_strides[3];   /* (batch, head, token) strides of Q_r in elements */
+  int64_t kv_strides[3];  /* (batch, head, token) strides of K_j and V_j in elements */
+  void* stream;           /* hipStream_t for all enqueued work */
+} ra_desc;
+
+/* Counts, summed over every (batch, query head) a launch covers.  live_pairs counts
+ * allowed (query, key) pairs, so useful FLOPs = 4 * head_dim * live_pairs. */
+typedef struct ra_stats {
+  int64_t live_pairs;
+  int64_t tiles_full;      /* (query tile, key tile) pairs computed without a mask */
+  int64_t tiles_partial;   /* computed with the element mask (tile crosses the diagonal) */
+  int64_t tiles_empty;     /* skipped: no allowed pair */
+  int64_t blocks_run;      /* ra_block_step calls that launched the step kernel */
+  int64_t blocks_skipped;  /* ra_block_step calls whose block held no allowed pair */
+  int32_t tile_q;          /* query rows per tile of the kernel that runs this desc */
+  int32_t tile_k;          /* keys per tile */
+} ra_stats;
+
+typedef struct ra_state ra_state; /* opaque, host-side, owned by the library */
+
+/* ---- state buffer ---------------------------------------------------------------- */
+
+/* Bytes of device workspace that holds the state (O~, m, l) for desc; 0 if desc is
+ * invalid or q_len == 0.  Layout (all fp32, 256-byte aligned sections):
+ *   O~ [B, Hq, n, d] at offset 0, m [B, Hq, n], l [B, Hq, n] at the offsets that
+ *   ra_workspace_layout reports.  m is kept in base-2 units: it is the reference
+ *   maximum of log2(e) * scale * <q, k> over the keys seen, and
+ *   l = sum 2^(log2(e)*scale*<q,k> - m), O~ = sum 2^(...) v.  A valid state satisfies
+ *   m >= max seen - 8, so every term stays <= 2^8. */
+size_t ra_workspace_bytes(const ra_desc* desc);
+
+/* Byte offsets of O~, m and l inside the workspace (host out-pointers, any may be NULL). */
+int ra_workspace_layout(const ra_desc* desc, size_t* o_off, size_t* m_off, size_t* l_off);
+
+/* ---- the lap ----------------------------------------------------------------------- */
+
+/* Bind the resident query slice Q_r (device, dtype desc.dtype) and a workspace of
+ * ra_workspace_bytes(desc) device bytes to a new state with m = -inf, l = 0, O~ = 0.
+ * Nothing is enqueued: the empty state is written by the first step that runs (or by
+ * ra_finalize if none runs), so the workspace may hold garbage until then.
+ * Q_r must stay valid and unchanged until ra_finalize's work has completed; the
+ * workspace belongs to the state until ra_state_destroy.  *out receives a host
+ * object to release with ra_state_destroy. */
+int ra_state_init(const ra_desc* desc, const void* q, void* workspace, ra_state** out);
+
+/* Like ra_state_init, but the workspace already holds a valid state (a checkpoint of a
+ * partial lap, e.g. a copy of another state's workspace); the lap continues from it. */
+int ra_state_resume(const ra_desc* desc, const void* q, void* workspace, ra_state** out);
+
+/* Score Q_r against one KV block of kv_len >= 0 keys (device K_j, V_j of dtype
+ * desc.dtype, strides desc.kv_strides) under mask_kind with the block's position
+ * offsets, and merge the result into the state.  A block with no allowed pair returns
+ * RA_OK without launching (counted in blocks_skipped).  K_j and V_j are read by work
+ * enqueued on desc.stream: the caller must not overwrite them until that work has
+ * completed (record an event after this call). */
+int ra_block_step(ra_state* st, const void* k, const void* v, int32_t kv_len,
+                  int32_t mask_kind, int64_t q_offset, int64_t k_offset);
+
+/* O_r = O~ / l, written as fp32 [B, Hq, n, d] contiguous (device), and, if lse is not
+ * NULL, lse = ln(sum over allowed keys of exp(scale * <q,k>)) as fp32 [B, Hq, n]
+ * contiguous (device).  Rows that saw no allowed key give O = 0 and lse = -inf.
+ * Afterwards the state accepts no more steps (RA_E_STATE); a second finalize is also
+ * RA_E_STATE. */
+int ra_finalize(ra_state* st, float* o, float* lse);
+
+/* Release the host object (enqueues nothing; the workspace is the caller's). */
+int ra_state_destroy(ra_state* st);
+
+/* Host-side counts accumulated by the planner over this state's steps. */
+int ra_get_stats(const ra_state* st, ra_stats* out);
+
+/* Debug: when counters is a device pointer to 3 zeroed uint64 values, every later step
+ * of this state runs the counting variant of its kernel, which adds (atomically, on the
+ * device) the tiles it computed unmasked, the tiles it computed masked and the allowed
+ * pairs it actually scored.  NULL switches counting off. */
+int ra_state_set_debug_counters(ra_state* st, uint64_t* counters);
+
+/* ---- host-only planner (no device work; safe without a GPU) ------------------------ */
+
+/* What ra_block_step would do for this block, as counts for the whole launch. */
+int ra_plan_block(const ra_desc* desc, int32_t kv_len, int32_t mask_kind,
+                  int64_t q_offset, int64_t k_offset, ra_stats* out);
+
+/* Class of every (query tile, key tile) of one head for this block, row-major
+ * [ceil(q_len/tile_q)][ceil(kv_len/tile_k)] into host memory host_out of cap bytes,
+ * using the kernel's own tile sizes (reported by ra_plan_block). */
+int ra_tile_classes(const ra_desc* desc, int32_t kv_len, int32_t mask_kind,
+                    int64_t q_offset, int64_t k_offset, uint8_t* host_out, size_t cap);
+
+/* ---- emulated ring on one GPU ----------------------------------------------------- */
+
+/* One whole lap for rank `rank` of a ring of desc.ring_size ranks, on one GPU.  The P
+ * blocks sit in device memory (k_blocks[j], v_blocks[j]: host arrays of P device
+ * pointers, each block kv_len keys in desc.kv_strides layout and block_bytes bytes
+ * contiguous).  Step 0 uses the rank's own block in place; for every later step the
+ * block (rank - s) mod P is copied into one of two receive buffers with hipMemcpyAsync
+ * on side_stream while the previous step's kernel runs on desc.stream; events order
+ * copy-after-consume and compute-after-arrival ("GPU ring attention", section "Hiding the
+ * ring behind the GEMMs"; charlestar page, section 双缓冲是重叠成立的基础).
+ * recv_k[2], recv_v[2] are the receive buffers (block_bytes each).  Positions follow
+ * mask_kind (contiguous: rank * q_len and j * kv_len; striped: rank and j).  Writes O
+ * and lse as ra_finalize does; stats_out (host, may be NULL) receives the lap's counts.
+ * The workspace is used as the state.  Events are created and destroyed per call. */
+typedef struct ra_lap {
+  const void* const* k_blocks;  /* host array [P] of device pointers */
+  const void* const* v_blocks;  /* host array [P] of device pointers */
+  void* recv_k[2];              /* device receive buffers */
+  void* recv_v[2];
+  size_t block_bytes;           /* bytes copied per K (and per V) block */
+  int32_t rank;                 /* 0 <= rank < P */
+  int32_t kv_len;               /* keys per block */
+  int32_t mask_kind;
+  int32_t poison;               /* nonzero: fill each receive buffer with NaN before its copy */
+  void* side_stream;            /* hipStream_t for the emulated transfers */
+  void* const* step_events;     /* NULL, or host array [2P] of hipEvent_t created by the caller:
+                                   [2s] is recorded on desc.stream just before step s's kernel
+                                   (after its wait for the block) and [2s+1] just after it */
+} ra_lap;
+
+int ra_ring_lap_emulated(const ra_desc* desc, const void* q, void* workspace,
+                         const ra_lap* lap, float* o, float* lse, ra_stats* stats_out);
+
+/* ---- misc ------------------------------------------------------------------------ */
+const char* ra_status_string(int status);
+int ra_version(void); /* ABI version, currently 1 */
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* RA_H_ */

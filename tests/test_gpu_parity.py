@@ -1,0 +1,274 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 oracle.
+
+Sizes here let the oracle compute every output element, span several tiles
+and end on ragged tails.  Full-size workloads are in test_gpu_fullsize.py.
+"""
+
+import math
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from gpu_util import (assert_bf16_close, assert_f32_close, lap_with_steps, require_gpu, say,
+                      to64)
+
+pytestmark = pytest.mark.gpu
+
+NONE, CONTIG, STRIPED = 0, 1, 2
+LAYOUT = {NONE: "contiguous", CONTIG: "contiguous", STRIPED: "striped"}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    require_gpu()
+    import exact_long_context_amd  # noqa: F401
+    yield
+    torch.cuda.synchronize()
+
+
+def _blocks(k, v, P, layout, dev="cuda"):
+    from exact_long_context_amd.workload import shard_blocks
+    return shard_blocks(k.to(dev), v.to(dev), P, layout)
+
+
+# ---------------------------------------------------------------------------
+# tiny exactness workload: N=256, P=4, one head, d=64, fp32
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("mask", [NONE, CONTIG])
+@pytest.mark.parametrize("rank", [0, 1, 2, 3])
+def test_tiny_fp32_workload(mask, rank):
+    w = synth.WORKLOADS["tiny_fp32_n256_p4"]
+    q_all, k, v = synth.workload_tensors(w, rank)
+    n = w.n_local
+    q_pos = oracle.tokens_of_rank(w.N, w.P, "contiguous", rank)
+    q = q_all[:, :, q_pos].contiguous()
+    kb, vb = _blocks(k, v, w.P, "contiguous")
+    say(f"  tiny fp32 rank={rank} mask={mask}")
+    o, lse, stats = lap_with_steps(q.cuda(), kb, vb, rank, mask, w.P)
+    torch.cuda.synchronize()
+    ref, ref_lse = oracle.dense_attention(to64(q), to64(k), to64(v), q_pos, np.arange(w.N), mask != NONE)
+    assert_f32_close(to64(o), ref, f"O rank {rank}")
+    fin = np.isfinite(ref_lse)
+    assert np.array_equal(np.isfinite(to64(lse)), fin)
+    assert np.max(np.abs(to64(lse)[fin] - ref_lse[fin])) <= 1e-5 * max(1.0, np.max(np.abs(ref_lse)))
+    pairs = oracle.live_pair_count(q_pos, np.arange(w.N), mask != NONE)
+    assert stats["live_pairs"] == pairs
+    if mask == CONTIG:
+        assert stats["blocks_skipped"] == w.P - 1 - rank
+
+
+# ---------------------------------------------------------------------------
+# random small shapes: both dtypes, GQA, every mask, ragged tails
+# ---------------------------------------------------------------------------
+
+CASES = [
+    # dtype, B, Hq, Hkv, d, N, P, rank, mask
+    ("bf16", 1, 2, 2, 128, 1024, 4, 2, NONE),
+    ("bf16", 2, 4, 2, 128, 1200, 4, 3, CONTIG),      # 300-token blocks: ragged tiles
+    ("bf16", 1, 8, 1, 128, 1024, 8, 5, STRIPED),     # GQA 8:1
+    ("bf16", 1, 4, 4, 64, 800, 4, 1, STRIPED),       # d = 64, 200-token blocks
+    ("bf16", 2, 6, 3, 64, 1000, 2, 1, CONTIG),       # 500-token blocks
+    ("bf16", 1, 2, 1, 128, 4 * 1037, 4, 3, CONTIG),  # odd block length
+    ("f32", 1, 2, 1, 128, 768, 4, 2, STRIPED),
+    ("f32", 2, 4, 2, 64, 600, 3, 1, CONTIG),         # 200-token blocks
+    ("f32", 1, 3, 3, 128, 500, 5, 4, NONE),          # 100-token blocks
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[f"{c[0]}-B{c[1]}-H{c[2]}x{c[3]}-d{c[4]}-N{c[5]}-P{c[6]}-r{c[7]}-m{c[8]}"
+                                             for c in CASES])
+def test_random_small_lap(case):
+    dtype, B, Hq, Hkv, d, N, P, rank, mask = case
+    layout = LAYOUT[mask]
+    seed = zlib.crc32(repr(case).encode()) % 1000
+    q_pos = oracle.tokens_of_rank(N, P, layout, rank)
+    n = q_pos.size
+    q, k, v = synth.random_case(seed, B, Hq, Hkv, n, N, d, dtype)
+    kb, vb = _blocks(k, v, P, layout)
+    say(f"  case {case}")
+    o, lse, stats = lap_with_steps(q.cuda(), kb, vb, rank, mask, P)
+    torch.cuda.synchronize()
+    ref, ref_lse = oracle.dense_attention(to64(q), to64(k), to64(v), q_pos, np.arange(N), mask != NONE)
+    got = to64(o)
+    assert np.isfinite(got).all()
+    if dtype == "bf16":
+        assert_bf16_close(got, ref, "O")
+    else:
+        assert_f32_close(got, ref, "O")
+    fin = np.isfinite(ref_lse)
+    assert np.array_equal(np.isfinite(to64(lse)), fin)
+    assert np.max(np.abs(to64(lse)[fin] - ref_lse[fin])) <= (2e-2 if dtype == "bf16" else 1e-5) * \
+        max(1.0, float(np.max(np.abs(ref_lse[fin]))))
+    assert stats["live_pairs"] == B * Hq * oracle.live_pair_count(q_pos, np.arange(N), mask != NONE)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("mask", [CONTIG, STRIPED])
+def test_mask_and_skip_decisions_bit_exact(dtype, mask):
+    """The kernel's own counts of unmasked tiles, masked tiles and scored pairs equal the
+    oracle's enumeration with the kernel's tile sizes, block by block."""
+    import exact_long_context_amd as ra
+    N, P, rank, Hq = 2048, 4, 2, 2
+    layout = LAYOUT[mask]
+    q_pos = oracle.tokens_of_rank(N, P, layout, rank)
+    n = q_pos.size
+    q, k, v = synth.random_case(7, 1, Hq, 1, n, N, 128, dtype)
+    kb, vb = _blocks(k, v, P, layout)
+    qd = q.cuda()
+    for j in range(P):
+        kp = oracle.tokens_of_rank(N, P, layout, j)
+        counters = torch.zeros(3, dtype=torch.int64, device="cuda")
+        st = ra.RingState(qd, kb[0], ring_size=P)
+        st.set_debug_counters(counters)
+        qo, ko = ra.block_offsets(mask, rank, j, n, n)
+        st.step(kb[j], vb[j], mask, qo, ko)
+        plan = st.stats()
+        st.finalize()
+        torch.cuda.synchronize()
+        c = counters.cpu().tolist()
+        cls = oracle.tile_classes(q_pos, kp, plan["tile_q"], plan["tile_k"], True)
+        want = [Hq * int((cls == oracle.FULL).sum()), Hq * int((cls == oracle.PARTIAL).sum()),
+                Hq * oracle.live_pair_count(q_pos, kp, True)]
+        say(f"    block {j}: kernel {c} oracle {want}")
+        if want[2] == 0:
+            assert c == [0, 0, 0] and plan["blocks_skipped"] == 1
+        else:
+            assert c == want
+        st.close()
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("layout,mask", [("contiguous", CONTIG), ("striped", STRIPED)])
+def test_single_visible_key_row_is_exact(dtype, layout, mask):
+    """Global position 0 (rank 0, local row 0) may see only key 0: O = V[key 0] exactly."""
+    N, P, d = 1024, 4, 128
+    q_pos = oracle.tokens_of_rank(N, P, layout, 0)
+    q, k, v = synth.random_case(11, 1, 2, 1, q_pos.size, N, d, dtype)
+    kb, vb = _blocks(k, v, P, layout)
+    o, lse, _ = lap_with_steps(q.cuda(), kb, vb, 0, mask, P)
+    torch.cuda.synchronize()
+    got = o[0, :, 0].cpu()
+    want = v[0, 0, 0].to(torch.float32).expand_as(got)
+    assert torch.equal(got, want)
+
+
+def test_order_invariance_and_state_resume_bitwise():
+    import exact_long_context_amd as ra
+    N, P, rank = 2048, 4, 1
+    q_pos = oracle.tokens_of_rank(N, P, "striped", rank)
+    q, k, v = synth.random_case(13, 1, 4, 2, q_pos.size, N, 128, "bf16")
+    kb, vb = _blocks(k, v, P, "striped")
+    qd = q.cuda()
+    base, _, _ = lap_with_steps(qd, kb, vb, rank, STRIPED, P)
+    rev, _, _ = lap_with_steps(qd, kb, vb, rank, STRIPED, P, order=list(reversed(oracle.ring_visit_order(P, rank))))
+    ref, _ = oracle.dense_attention(to64(q), to64(k), to64(v), q_pos, np.arange(N), True)
+    assert_bf16_close(to64(rev), ref, "reversed order")
+    # checkpoint after two blocks, resume from a copy of the workspace, finish: bit-identical
+    order = oracle.ring_visit_order(P, rank)
+    n = q_pos.size
+    st = ra.RingState(qd, kb[0], ring_size=P)
+    for j in order[:2]:
+        st.step(kb[j], vb[j], STRIPED, *ra.block_offsets(STRIPED, rank, j, n, n))
+    saved = st.workspace.clone()
+    st.close()
+    st2 = ra.RingState(qd, kb[0], ring_size=P, workspace=saved, resume=True)
+    for j in order[2:]:
+        st2.step(kb[j], vb[j], STRIPED, *ra.block_offsets(STRIPED, rank, j, n, n))
+    o2, _ = st2.finalize()
+    torch.cuda.synchronize()
+    assert torch.equal(o2, base)
+    # the exported state satisfies its invariant: m is the running max (base 2) per row
+    st3 = ra.RingState(qd, kb[0], ring_size=P)
+    for j in order:
+        st3.step(kb[j], vb[j], STRIPED, *ra.block_offsets(STRIPED, rank, j, n, n))
+    torch.cuda.synchronize()
+    o_acc, m, l_ = (t.cpu().double().numpy() for t in st3.state_views())
+    s = np.einsum("hid,htd->hit", to64(q)[0], np.repeat(to64(k)[0], 2, axis=0)) / math.sqrt(128)
+    ok = oracle.allowed_mask(q_pos, np.arange(N), True)
+    xmax = np.where(ok, s, -np.inf).max(axis=-1) * math.log2(math.e)
+    assert np.all(m[0] >= xmax - 8.0) and np.all(m[0] <= xmax + 1e-3)
+    st3.close()
+
+
+def test_emulated_ring_lap_matches_steps_and_poison():
+    import exact_long_context_amd as ra
+    N, P = 4096, 8
+    for mask, rank in ((NONE, 3), (CONTIG, 6), (STRIPED, 5)):
+        layout = LAYOUT[mask]
+        q_pos = oracle.tokens_of_rank(N, P, layout, rank)
+        q, k, v = synth.random_case(17 + mask, 1, 4, 4, q_pos.size, N, 128, "bf16")
+        kb, vb = _blocks(k, v, P, layout)
+        qd = q.cuda()
+        o_steps, lse_steps, st_steps = lap_with_steps(qd, kb, vb, rank, mask, P)
+        ring = ra.EmulatedRing(kb, vb)
+        o_ring, lse_ring, st_ring = ring.lap(qd, rank, mask)
+        o_pois, lse_pois, _ = ring.lap(qd, rank, mask, poison=True)
+        torch.cuda.synchronize()
+        say(f"  emulated lap mask={mask} rank={rank} stats={st_ring}")
+        assert torch.equal(o_ring, o_steps) and torch.equal(o_pois, o_steps)
+        assert torch.equal(lse_ring, lse_steps) and torch.equal(lse_pois, lse_steps)
+        assert st_ring == st_steps
+
+
+def test_degenerate_inputs():
+    import exact_long_context_amd as ra
+    # empty query slice
+    q = torch.empty((1, 2, 0, 128), dtype=torch.bfloat16, device="cuda")
+    k = torch.randn((1, 2, 64, 128), device="cuda").to(torch.bfloat16)
+    st = ra.RingState(q, k, ring_size=2)
+    st.step(k, k, NONE)
+    o, lse = st.finalize()
+    assert o.numel() == 0
+    st.close()
+    # every block strictly in the future (a partial lap of rank 0): O = 0, lse = -inf
+    q = torch.randn((1, 2, 100, 128), device="cuda").to(torch.bfloat16)
+    st = ra.RingState(q, k, ring_size=4)
+    for j in (1, 2, 3):
+        st.step(k, k, CONTIG, 0, j * 100)
+    o, lse = st.finalize()
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(o).item() == 0 and torch.isneginf(lse).all()
+    assert st.stats()["blocks_run"] == 0
+    st.close()
+    # zero-length blocks are no-ops
+    st = ra.RingState(q, k, ring_size=4)
+    st.step(k[:, :, :0], k[:, :, :0], NONE)
+    st.step(k, k, NONE)
+    o, _ = st.finalize()
+    st2 = ra.RingState(q, k, ring_size=4)
+    st2.step(k, k, NONE)
+    o2, _ = st2.finalize()
+    torch.cuda.synchronize()
+    assert torch.equal(o, o2)
+    st.close()
+    st2.close()
+    # a single-row, single-key lap
+    q1 = torch.randn((1, 1, 1, 64), device="cuda")
+    k1 = torch.randn((1, 1, 1, 64), device="cuda")
+    v1 = torch.randn((1, 1, 1, 64), device="cuda")
+    st = ra.RingState(q1, k1, ring_size=1)
+    st.step(k1, v1, CONTIG, 0, 0)
+    o, lse = st.finalize()
+    torch.cuda.synchronize()
+    assert torch.equal(o[0, 0, 0], v1[0, 0, 0])
+    st.close()
+
+
+def test_strided_views_without_copies():
+    """Q and KV given as [B, n, H, d] views (token-major) through the stride arguments."""
+    N, P, rank, Hq, Hkv, d = 1024, 4, 2, 4, 2, 128
+    q_pos = oracle.tokens_of_rank(N, P, "contiguous", rank)
+    q, k, v = synth.random_case(19, 1, Hq, Hkv, q_pos.size, N, d, "bf16")
+    n = q_pos.size
+    q_tm = q.permute(0, 2, 1, 3).contiguous().cuda().permute(0, 2, 1, 3)   # strides (n*H*d, d, H*d)
+    kb = [k[:, :, j * n:(j + 1) * n].permute(0, 2, 1, 3).contiguous().cuda().permute(0, 2, 1, 3) for j in range(P)]
+    vb = [v[:, :, j * n:(j + 1) * n].permute(0, 2, 1, 3).contiguous().cuda().permute(0, 2, 1, 3) for j in range(P)]
+    o, _, _ = lap_with_steps(q_tm, kb, vb, rank, CONTIG, P)
+    torch.cuda.synchronize()
+    ref, _ = oracle.dense_attention(to64(q), to64(k), to64(v), q_pos, np.arange(N), True)
+    assert_bf16_close(to64(o), ref, "token-major views")
