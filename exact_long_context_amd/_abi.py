@@ -109,12 +109,30 @@ class RaError(RuntimeError):
         self.code = code
 
 
+def _hip_runtimes_mapped() -> set:
+    """Distinct HIP runtime files mapped into this process."""
+    try:
+        with open("/proc/self/maps") as f:
+            return {os.path.realpath(ln.split()[-1]) for ln in f if "libamdhip64" in ln}
+    except OSError:
+        return set()
+
+
 def load(path: str = LIB_PATH) -> C.CDLL:
     if not os.path.exists(path):
         raise ImportError(
             f"{path} is missing: build it with `python -m exact_long_context_amd.build` "
             "(there is no fallback implementation)")
+    # One HIP runtime per process: torch ships its own libamdhip64 (soname
+    # libamdhip64.so.7).  Loading torch first lets the library's NEEDED entry bind to
+    # that copy; loading the library first would map /opt/rocm's copy as well, and
+    # torch's streams would then be handed to a different runtime.
+    import torch  # noqa: F401
     lib = C.CDLL(path)
+    runtimes = _hip_runtimes_mapped()
+    if len(runtimes) > 1:
+        raise ImportError(f"two HIP runtimes are mapped in this process: {sorted(runtimes)}; "
+                          "import torch before anything that loads /opt/rocm's libamdhip64")
     for name, (res, args) in SIGNATURES.items():
         fn = getattr(lib, name)
         fn.restype = res

@@ -239,3 +239,10 @@ def test_lap_argument_validation():
     assert lib.ra_ring_lap_emulated(C.byref(d), 0x10000, 0x20000, C.byref(lap), 0x50000, None,
                                     None) == ra.RA_E_INVALID
     assert lib.ra_ring_lap_emulated(None, 0, 0, None, 0, None, None) == ra.RA_E_INVALID
+
+
+def test_one_hip_runtime_per_process():
+    """The library binds to the HIP runtime torch ships; a second copy of libamdhip64 in
+    the process would receive torch's stream handles and crash."""
+    import torch  # noqa: F401
+    assert len(_abi._hip_runtimes_mapped()) == 1

@@ -1,7 +1,7 @@
 """GPU parity: the HIP path through the C ABI against the fp64 oracle.
 
 Sizes here let the oracle compute every output element, span several tiles
-and end on ragged tails.  Full-size workloads are in test_gpu_fullsize.py.
+and end on ragged tails.  Full-size workloads are in test_gpu_sampled_fullsize.py.
 """
 
 import math
