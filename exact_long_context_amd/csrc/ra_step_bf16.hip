@@ -33,6 +33,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "ra_internal.h"
 #include "ra_pos.h"
 
@@ -62,9 +64,11 @@ template <int D>
 __device__ __forceinline__ int k_off(int t, int c) {
   return t * (D * 2) + ((c ^ (t & 7)) << 4);
 }
-// byte offset of chunk ch (= 2*kk + h, eight keys) of value row dv in the V^T tile
+// byte offset of chunk ch (= 2*kk + h, eight keys) of value row dv in the V^T tile; the
+// swizzle depends on dv mod 32 only, so the four 32-row blocks differ by a constant
 __device__ __forceinline__ int v_off(int dv, int ch) {
-  return dv * (BK * 2) + ((ch ^ ((dv + (dv >> 3)) & 7)) << 4);
+  const int r = dv & 31;
+  return dv * (BK * 2) + ((ch ^ ((r + (r >> 3)) & 7)) << 4);
 }
 
 // (value of this lane, value of lane ^ 32) in either order: enough for max and sum
@@ -74,14 +78,27 @@ __device__ __forceinline__ void pair32(float x, float& a, float& b) {
   b = __uint_as_float(r[1]);
 }
 
+// Buffer resource over [base, base + bytes): loads past the end return zero, which is how
+// the tail of a block is padded without branches.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  const int n = bytes > 0x7fffffff ? 0x7fffffff : (int)(bytes < 0 ? 0 : bytes);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, 0x00020000);
+}
+
+// The running maximum may lag the true one by up to this much (base 2) before O~ and l are
+// rescaled: every term 2^(x - m) then stays <= 2^8, and most tiles skip the rescale.
+constexpr float kLagMax = 8.0f;
+
 template <int D, bool DEBUG>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void step_bf16_kernel(StepParams p) {
   constexpr int KS = D / 16;           // k-steps of the score contraction
   constexpr int VB = D / 32;           // 32-wide blocks of the value dimension
-  constexpr int KPT = BK * D / 8 / NT; // 16-byte K chunks staged per thread
-  constexpr int VTASKS = 2 * D;        // (4 key groups x 2 halves) x D/4 dim groups
-  __shared__ __attribute__((aligned(16))) unsigned char lds[2 * Lds<D>::BUF];
+  constexpr int KCH = D / 8;           // 16-byte chunks per K row
+  constexpr int KPT = BK * KCH / NT;   // 16-byte K chunks staged per thread
+  constexpr int KROWS = NT / KCH;      // K rows covered by one staging pass of the workgroup
+  constexpr int BUF = Lds<D>::BUF;
+  __shared__ __attribute__((aligned(16))) unsigned char lds[2 * BUF];
   __shared__ unsigned long long dbg_acc;
 
   const int tid = threadIdx.x;
@@ -159,72 +176,68 @@ void step_bf16_kernel(StepParams p) {
   // ---- staging: global -> registers -> LDS -------------------------------------------
   const __bf16* kg = static_cast<const __bf16*>(p.k) + (int64_t)b * p.k_sb + (int64_t)kvh * p.k_sh;
   const __bf16* vg = static_cast<const __bf16*>(p.v) + (int64_t)b * p.k_sb + (int64_t)kvh * p.k_sh;
-  const bool v_task = tid < VTASKS;
-  const int vdg = tid % (D / 4);       // value dims 4*vdg .. 4*vdg+3
-  const int vkh = (tid / (D / 4)) & 7; // key group kk = vkh>>1, half h = vkh&1
+  const int row_bytes = (int)(p.k_st * 2);        // host guarantees BK rows fit in 31 bits
+  // K: thread stages chunk (tid % KCH) of rows tid / KCH + u * KROWS
+  const int k_goff = (tid / KCH) * row_bytes + (tid % KCH) * 16;
+  const int k_woff = k_off<D>(tid / KCH, tid % KCH);   // + u * KROWS rows (a multiple of 8)
+  // V: thread stages value dims 4*vdg..4*vdg+3 of the eight keys of group vkh (kk = vkh>>1,
+  // half = vkh&1), in the permuted key order of the score layout; for D = 64 two threads
+  // share each task and write identical data
+  const int vdg = tid % (D / 4);
+  const int vkh = (tid / (D / 4)) & 7;
+  const int v_goff = (16 * (vkh >> 1) + 4 * (vkh & 1)) * row_bytes + vdg * 8;
+  int v_woff[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) v_woff[e] = Lds<D>::K_BYTES + v_off(vdg * 4 + e, vkh);
+  // operand reads: loop-invariant per lane
+  int k_roff[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) k_roff[ks] = k_off<D>(r32, 2 * ks + hi);
+  int v_roff[4];
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) v_roff[kk] = Lds<D>::K_BYTES + v_off(r32, 2 * kk + hi);
+
   u32x4 kreg[KPT];
   u32x2 vreg[8];
 
   auto load_tile = [&](int kt) {
-    const int t0 = kt * BK;
+    const int64_t t0 = (int64_t)kt * BK;
+    const int64_t bytes = ((int64_t)p.n_k - t0) * p.k_st * 2;
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(kg + t0 * p.k_st, bytes);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(vg + t0 * p.k_st, bytes);
 #pragma unroll
-    for (int u = 0; u < KPT; ++u) {
-      const int ci = tid + NT * u;
-      const int t = ci / (D / 8), c = ci % (D / 8);
-      if (t0 + t < p.n_k)
-        kreg[u] = *reinterpret_cast<const u32x4*>(kg + (int64_t)(t0 + t) * p.k_st + c * 8);
-      else
-        kreg[u] = u32x4{0u, 0u, 0u, 0u};
-    }
-    if (v_task) {
+    for (int u = 0; u < KPT; ++u)
+      kreg[u] = __builtin_amdgcn_raw_buffer_load_b128(rk, k_goff, u * KROWS * row_bytes, 0);
 #pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        const int key = 16 * (vkh >> 1) + 4 * (vkh & 1) + (q & 3) + 8 * (q >> 2);
-        if (t0 + key < p.n_k)
-          vreg[q] = *reinterpret_cast<const u32x2*>(vg + (int64_t)(t0 + key) * p.k_st + vdg * 4);
-        else
-          vreg[q] = u32x2{0u, 0u};
-      }
+    for (int q = 0; q < 8; ++q)
+      vreg[q] = __builtin_amdgcn_raw_buffer_load_b64(rv, v_goff, ((q & 3) + 8 * (q >> 2)) * row_bytes, 0);
+  };
+  auto store_tile = [&](auto bufc) {
+    constexpr int B = decltype(bufc)::value;
+    unsigned char* base = lds + B * BUF;
+#pragma unroll
+    for (int u = 0; u < KPT; ++u)
+      *reinterpret_cast<u32x4*>(base + k_woff + u * KROWS * D * 2) = kreg[u];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const unsigned sel = (e & 1) ? 0x07060302u : 0x05040100u;
+      u32x4 w;
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+        w[m] = __builtin_amdgcn_perm(vreg[2 * m + 1][e >> 1], vreg[2 * m][e >> 1], sel);
+      *reinterpret_cast<u32x4*>(base + v_woff[e]) = w;
     }
   };
-  auto store_tile = [&](int buf) {
-    unsigned char* kb = lds + buf * Lds<D>::BUF;
-    unsigned char* vb = kb + Lds<D>::K_BYTES;
-#pragma unroll
-    for (int u = 0; u < KPT; ++u) {
-      const int ci = tid + NT * u;
-      const int t = ci / (D / 8), c = ci % (D / 8);
-      *reinterpret_cast<u32x4*>(kb + k_off<D>(t, c)) = kreg[u];
-    }
-    if (v_task) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const unsigned sel = (e & 1) ? 0x07060302u : 0x05040100u;
-        u32x4 w;
-#pragma unroll
-        for (int m = 0; m < 4; ++m)
-          w[m] = __builtin_amdgcn_perm(vreg[2 * m + 1][e >> 1], vreg[2 * m][e >> 1], sel);
-        *reinterpret_cast<u32x4*>(vb + v_off(vdg * 4 + e, vkh)) = w;
-      }
-    }
-  };
-
-  if (kt_live > 0) {
-    load_tile(0);
-    store_tile(0);
-  }
-  __syncthreads();
 
   const float c2 = p.scale_log2;
   unsigned long long my_pairs = 0;
 
-  for (int kt = 0; kt < kt_live; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < kt_live) load_tile(kt + 1);
-    const unsigned char* kb = lds + cur * Lds<D>::BUF;
-    const unsigned char* vb = kb + Lds<D>::K_BYTES;
+  // one key tile from LDS buffer B: scores, mask, online softmax, value product
+  auto compute_tile = [&](auto bufc, int kt) {
+    constexpr int B = decltype(bufc)::value;
+    const unsigned char* base = lds + B * BUF;
 
-    // S^T = K Q^T: lane holds keys 8*(j/4) + 4*hi + (j%4) (+32*kb) of query row r32
+    // S^T = K Q^T: lane holds keys 8*(j/4) + 4*hi + (j%4) (+32*kh) of query row r32
     f32x16 sacc[2];
 #pragma unroll
     for (int kh = 0; kh < 2; ++kh)
@@ -234,20 +247,19 @@ void step_bf16_kernel(StepParams p) {
     for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
       for (int kh = 0; kh < 2; ++kh) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(kb + k_off<D>(kh * 32 + r32, 2 * ks + hi));
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(base + k_roff[ks] + kh * 32 * D * 2);
         sacc[kh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], sacc[kh], 0, 0, 0);
       }
     }
 
     // element mask on tiles that cross the diagonal or run past the block's end
-    const bool masked = (kt >= kt_full) || ((kt + 1) * BK > p.n_k);
-    if (masked) {
+    if ((kt >= kt_full) || ((kt + 1) * BK > p.n_k)) {
       const int lim = min(qrow + p.diag, p.n_k - 1) - kt * BK - 4 * hi;
 #pragma unroll
       for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
         for (int j = 0; j < 16; ++j)
-          if (kh * 32 + 8 * (j >> 2) + (j & 3) > lim) sacc[kh][j] = -INFINITY;
+          sacc[kh][j] = (kh * 32 + 8 * (j >> 2) + (j & 3) > lim) ? -INFINITY : sacc[kh][j];
     }
     if (DEBUG && row_ok) {
 #pragma unroll
@@ -267,9 +279,22 @@ void step_bf16_kernel(StepParams p) {
       pair32(mx, a, bb);
       mx = fmaxf(a, bb);
     }
-    const float m_new = fmaxf(m_run, mx * c2);
-    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+    // move the reference maximum only when some row of the wave grew by more than kLagMax
+    const float m_tile = mx * c2;
+    const bool grow = m_tile > m_run + kLagMax;
+    if (__builtin_amdgcn_ballot_w64(grow)) {
+      // rows that do not grow keep their reference (alpha = 1; this also keeps a row that
+      // has seen no key yet at -inf without forming -inf - -inf); a growing row from
+      // -inf gets alpha = 0 on its empty accumulators
+      const float alpha = grow ? __builtin_amdgcn_exp2f(m_run - m_tile) : 1.0f;
+      l_run *= alpha;
+#pragma unroll
+      for (int vb2 = 0; vb2 < VB; ++vb2)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) oacc[vb2][j] *= alpha;
+      m_run = grow ? m_tile : m_run;
+    }
+    const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
 
     // probabilities, rounded to bf16: the B operand of the value product; the row sum
     // adds the same rounded values (v_dot2 with ones), so the weights used for O~ and for
@@ -297,25 +322,38 @@ void step_bf16_kernel(StepParams p) {
       pair32(rs, a, bb);
       rs = a + bb;
     }
-    l_run = l_run * alpha + rs;
-    m_run = m_new;
-#pragma unroll
-    for (int vb2 = 0; vb2 < VB; ++vb2)
-#pragma unroll
-      for (int j = 0; j < 16; ++j) oacc[vb2][j] *= alpha;
+    l_run += rs;
 
     // O~^T += V^T P^T
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
 #pragma unroll
       for (int vb2 = 0; vb2 < VB; ++vb2) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(vb + v_off(vb2 * 32 + r32, 2 * kk + hi));
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(base + v_roff[kk] + vb2 * 32 * BK * 2);
         oacc[vb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pk[kk], oacc[vb2], 0, 0, 0);
       }
     }
+  };
 
-    if (kt + 1 < kt_live) store_tile(cur ^ 1);
+  // one pipeline step: prefetch tile kt+1 to registers, compute tile kt from buffer B,
+  // stage tile kt+1 into the other buffer, barrier.  The prefetch and the staging are
+  // unconditional (after the last live tile they fetch zeros or unused keys into the idle
+  // buffer): with no branch around them the loads are waited for only at the LDS stores,
+  // so the whole tile computation overlaps them.
+  auto step = [&](auto bufc, int kt) {
+    constexpr int B = decltype(bufc)::value;
+    load_tile(kt + 1);
+    compute_tile(bufc, kt);
+    store_tile(std::integral_constant<int, 1 - B>{});
     __syncthreads();
+  };
+
+  load_tile(0);
+  store_tile(std::integral_constant<int, 0>{});
+  __syncthreads();
+  for (int kt = 0; kt < kt_live; kt += 2) {
+    step(std::integral_constant<int, 0>{}, kt);
+    if (kt + 1 < kt_live) step(std::integral_constant<int, 1>{}, kt + 1);
   }
 
   // ---- write the state back ----------------------------------------------------------

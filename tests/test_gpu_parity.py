@@ -108,6 +108,32 @@ def test_random_small_lap(case):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("mask,rank", [(STRIPED, 1), (STRIPED, 6), (CONTIG, 5), (NONE, 2)])
+def test_lap_in_shuffled_block_order(dtype, mask, rank):
+    """Blocks in a seeded random order: the first blocks may leave rows with no visible key
+    (striped blocks after the rank's own), which the state must carry through unchanged."""
+    N, P, Hq, Hkv = 2048, 8, 4, 2
+    layout = LAYOUT[mask]
+    q_pos = oracle.tokens_of_rank(N, P, layout, rank)
+    q, k, v = synth.random_case(23 + rank, 1, Hq, Hkv, q_pos.size, N, 128, dtype)
+    kb, vb = _blocks(k, v, P, layout)
+    order = [int(j) for j in np.random.default_rng(rank).permutation(P)]
+    if mask == STRIPED:   # start with a block that sees strictly fewer keys than the rows
+        order.remove(P - 1)
+        order.insert(0, P - 1)
+    say(f"  order {order}")
+    o, lse, _ = lap_with_steps(q.cuda(), kb, vb, rank, mask, P, order=order)
+    torch.cuda.synchronize()
+    ref, ref_lse = oracle.dense_attention(to64(q), to64(k), to64(v), q_pos, np.arange(N), mask != NONE)
+    got = to64(o)
+    assert np.isfinite(got).all()
+    if dtype == "bf16":
+        assert_bf16_close(got, ref, "O")
+    else:
+        assert_f32_close(got, ref, "O")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("mask", [CONTIG, STRIPED])
 def test_mask_and_skip_decisions_bit_exact(dtype, mask):
     """The kernel's own counts of unmasked tiles, masked tiles and scored pairs equal the
