@@ -121,7 +121,7 @@ def _hip_runtimes_mapped() -> set:
 def load(path: str = LIB_PATH) -> C.CDLL:
     if not os.path.exists(path):
         raise ImportError(
-            f"{path} is missing: build it with `python -m exact_long_context_amd.build` "
+            f"{path} is missing: build it with `python exact_long_context_amd/build.py` "
             "(there is no fallback implementation)")
     # One HIP runtime per process: torch ships its own libamdhip64 (soname
     # libamdhip64.so.7).  Loading torch first lets the library's NEEDED entry bind to

@@ -1,6 +1,8 @@
 """Build librocring.so (the C-ABI library) for gfx950 with hipcc, in-tree.
 
-    python -m exact_long_context_amd.build
+    python exact_long_context_amd/build.py
+
+Run it by path (or load it by file): importing the package itself needs the library.
 
 Every source is compiled with packed-fp32 instruction selection switched off (the
 host pass of hipcc warns that it does not know that feature; that is harmless),
@@ -30,6 +32,9 @@ SOURCES = [
 ]
 
 ARCH = "gfx950"
+
+# Per-source extra compiler flags (none needed at present).
+EXTRA_FLAGS: dict[str, list[str]] = {}
 
 
 def _hipcc() -> str:
@@ -62,7 +67,7 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
     for src in SOURCES:
         obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
         objs.append(obj)
-        cmd = [hipcc] + compile_flags() + ["-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [hipcc] + compile_flags() + EXTRA_FLAGS.get(src, []) + ["-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)))
@@ -85,6 +90,13 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
     r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stdout.decode(errors="replace"))
+    # the library must load with every symbol resolved (a kernel whose host launch stub
+    # was not emitted shows up here, not at first use); checked in a child process so
+    # that this process maps no HIP runtime of its own
+    chk = subprocess.run([sys.executable, "-c", "import ctypes, sys; ctypes.CDLL(sys.argv[1])", tmp],
+                         stdout=subprocess.PIPE, stderr=subprocess.STDOUT)
+    if chk.returncode != 0:
+        raise RuntimeError("built library does not load:\n" + chk.stdout.decode(errors="replace"))
     os.replace(tmp, LIB)
     return LIB
 

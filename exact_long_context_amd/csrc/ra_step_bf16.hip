@@ -47,28 +47,46 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int BQ = kBf16TileQ;  // 128 query rows per workgroup
-constexpr int BK = kBf16TileK;  // 64 keys per LDS tile
+constexpr int BQ = kBf16TileQ;
+constexpr int BK = kBf16TileK;
 constexpr int NT = 256;         // 4 waves
 constexpr int WROWS = 32;       // query rows per wave
 
-template <int D>
-struct Lds {
-  static constexpr int K_BYTES = BK * D * 2;  // K tile [BK][D], row = D*2 bytes
-  static constexpr int V_BYTES = D * BK * 2;  // V^T tile [D][BK], row = 128 bytes
-  static constexpr int BUF = K_BYTES + V_BYTES;
-};
 
-// byte offset of 16-byte chunk c (dims 8c..8c+7) of key row t in the K tile
+// LDS banking on gfx950: 64 banks of 4 bytes (a 256-byte bank line).  A 16-byte-per-lane
+// access is served 16 lanes at a time and an 8-byte-per-lane access 32 lanes at a time, so
+// those lanes must touch distinct banks.
+//
+// Tiles are written straight from global memory into LDS (buffer_load ... lds: lane i of a
+// load writes bytes [16i, 16i+16) after the instruction's LDS base), so the swizzles below
+// are realised by choosing which 16-byte global chunk each lane fetches.
+
+// K tile [BK][D] bf16: physical 16-byte chunk of logical chunk c (dims 8c..8c+7) of key
+// row t.  The score operand read (16 consecutive rows at one chunk) hits 16 groups.
 template <int D>
-__device__ __forceinline__ int k_off(int t, int c) {
-  return t * (D * 2) + ((c ^ (t & 7)) << 4);
+__device__ __forceinline__ int k_phys(int t, int c) {
+  if constexpr (D == 128) return c ^ (t & 15);
+  else return c ^ ((t >> 1) & 7);
 }
-// byte offset of chunk ch (= 2*kk + h, eight keys) of value row dv in the V^T tile; the
-// swizzle depends on dv mod 32 only, so the four 32-row blocks differ by a constant
-__device__ __forceinline__ int v_off(int dv, int ch) {
-  const int r = dv & 31;
-  return dv * (BK * 2) + ((ch ^ ((r + (r >> 3)) & 7)) << 4);
+// V tile [BK][D] bf16, kept untransposed: the value operand is read with
+// ds_read_b64_tr_b16, whose 16-lane groups fetch four consecutive keys x four 8-byte
+// column pieces; the chunk twist below puts those 16 pieces (32 lanes: 256 bytes) on
+// distinct banks.
+template <int D>
+__device__ __forceinline__ int v_phys(int t, int c) {
+  if constexpr (D == 128) return c ^ (4 * (t & 3));
+  else return c ^ (4 * ((t >> 1) & 1));
+}
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __attribute__((address_space(3))) void lds_void;
+
+// 16 bytes per lane from a buffer straight into LDS at lds + 16 * lane (the LDS address is
+// taken from the first lane).  Kept out of the kernel template: the builtin has no host
+// form, and inside the template it would stop the host side from emitting the launch stub.
+__device__ __forceinline__ void load_lds_b128_inl(__amdgpu_buffer_rsrc_t r, void* lds, int voff, int soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 16, voff, soff, 0, 0);
 }
 
 // (value of this lane, value of lane ^ 32) in either order: enough for max and sum
@@ -89,21 +107,32 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, in
 // rescaled: every term 2^(x - m) then stays <= 2^8, and most tiles skip the rescale.
 constexpr float kLagMax = 8.0f;
 
+
 template <int D, bool DEBUG>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void step_bf16_kernel(StepParams p) {
-  constexpr int KS = D / 16;           // k-steps of the score contraction
-  constexpr int VB = D / 32;           // 32-wide blocks of the value dimension
-  constexpr int KCH = D / 8;           // 16-byte chunks per K row
-  constexpr int KPT = BK * KCH / NT;   // 16-byte K chunks staged per thread
-  constexpr int KROWS = NT / KCH;      // K rows covered by one staging pass of the workgroup
-  constexpr int BUF = Lds<D>::BUF;
-  __shared__ __attribute__((aligned(16))) unsigned char lds[2 * BUF];
+  constexpr int KS = D / 16;             // k-steps of the score contraction
+  constexpr int VB = D / 32;             // 32-wide blocks of the value dimension
+  constexpr int RB = D * 2;              // bytes per key row in LDS
+  constexpr int CPR = D / 8;             // 16-byte chunks per key row
+  constexpr int RPL = 64 / CPR;          // key rows per 1 KB direct load (one wave)
+  constexpr int LPW = BK * RB / 1024 / 4;  // direct loads per wave per tile, per tensor
+  // K tiles and V tiles, two of each, as separate objects so that the compiler can tell the
+  // tile being read from the one a direct load is filling.  K runs one tile ahead of V:
+  // while tile kt's probabilities are formed, tile kt+1's scores are on the matrix cores.
+  __shared__ __attribute__((aligned(16))) unsigned char k_t0[BK * D * 2];
+  __shared__ __attribute__((aligned(16))) unsigned char k_t1[BK * D * 2];
+  __shared__ __attribute__((aligned(16))) unsigned char v_t0[BK * D * 2];
+  __shared__ __attribute__((aligned(16))) unsigned char v_t1[BK * D * 2];
   __shared__ unsigned long long dbg_acc;
+  unsigned char* const k_tiles[2] = {k_t0, k_t1};
+  unsigned char* const v_tiles[2] = {v_t0, v_t1};
+#define ktile(bufc) (k_tiles[decltype(bufc)::value])
+#define vtile(bufc) (v_tiles[decltype(bufc)::value])
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar LDS bases
   const int r32 = lane & 31;
   const int hi = lane >> 5;
 
@@ -131,6 +160,44 @@ void step_bf16_kernel(StepParams p) {
   const int64_t srow = ((int64_t)b * p.q_heads + h) * p.n_q + qrow;
 
   if (DEBUG && tid == 0) dbg_acc = 0;
+
+  // ---- staging: global -> LDS directly ------------------------------------------------
+  const __bf16* kg = static_cast<const __bf16*>(p.k) + (int64_t)b * p.k_sb + (int64_t)kvh * p.k_sh;
+  const __bf16* vg = static_cast<const __bf16*>(p.v) + (int64_t)b * p.k_sb + (int64_t)kvh * p.k_sh;
+  const int row_bytes = (int)(p.k_st * 2);        // host guarantees BK rows fit in 31 bits
+  // Load u of wave w covers key rows (w*LPW + u)*RPL .. +RPL-1; lane -> (row, physical
+  // chunk) = (lane / CPR, lane % CPR) of that span; the global chunk is the inverse swizzle.
+  int k_goff[LPW], v_goff[LPW];
+#pragma unroll
+  for (int u = 0; u < LPW; ++u) {
+    const int t = (wave * LPW + u) * RPL + lane / CPR;
+    const int pc = lane % CPR;
+    int ck = 0, cv = 0;   // logical chunks whose physical slot is pc (the swizzles are involutions)
+    ck = k_phys<D>(t, pc);
+    cv = v_phys<D>(t, pc);
+    k_goff[u] = (lane / CPR) * row_bytes + ck * 16;
+    v_goff[u] = (lane / CPR) * row_bytes + cv * 16;
+  }
+  auto rsrc_of = [&](const __bf16* base, int kt) {
+    const int64_t t0 = (int64_t)kt * BK;
+    return make_rsrc(base + t0 * p.k_st, ((int64_t)p.n_k - t0) * p.k_st * 2);
+  };
+  auto load_k = [&](auto bufc, int kt) {
+    const __amdgpu_buffer_rsrc_t r = rsrc_of(kg, kt);
+#pragma unroll
+    for (int u = 0; u < LPW; ++u) {
+      const int row0 = (wave * LPW + u) * RPL;
+      load_lds_b128_inl(r, ktile(bufc) + row0 * RB, k_goff[u], row0 * row_bytes);
+    }
+  };
+  auto load_v = [&](auto bufc, int kt) {
+    const __amdgpu_buffer_rsrc_t r = rsrc_of(vg, kt);
+#pragma unroll
+    for (int u = 0; u < LPW; ++u) {
+      const int row0 = (wave * LPW + u) * RPL;
+      load_lds_b128_inl(r, vtile(bufc) + row0 * RB, v_goff[u], row0 * row_bytes);
+    }
+  };
 
   // ---- resident operands and state ---------------------------------------------------
   bf16x8 qf[KS];
@@ -173,72 +240,31 @@ void step_bf16_kernel(StepParams p) {
       }
   }
 
-  // ---- staging: global -> registers -> LDS -------------------------------------------
-  const __bf16* kg = static_cast<const __bf16*>(p.k) + (int64_t)b * p.k_sb + (int64_t)kvh * p.k_sh;
-  const __bf16* vg = static_cast<const __bf16*>(p.v) + (int64_t)b * p.k_sb + (int64_t)kvh * p.k_sh;
-  const int row_bytes = (int)(p.k_st * 2);        // host guarantees BK rows fit in 31 bits
-  // K: thread stages chunk (tid % KCH) of rows tid / KCH + u * KROWS
-  const int k_goff = (tid / KCH) * row_bytes + (tid % KCH) * 16;
-  const int k_woff = k_off<D>(tid / KCH, tid % KCH);   // + u * KROWS rows (a multiple of 8)
-  // V: thread stages value dims 4*vdg..4*vdg+3 of the eight keys of group vkh (kk = vkh>>1,
-  // half = vkh&1), in the permuted key order of the score layout; for D = 64 two threads
-  // share each task and write identical data
-  const int vdg = tid % (D / 4);
-  const int vkh = (tid / (D / 4)) & 7;
-  const int v_goff = (16 * (vkh >> 1) + 4 * (vkh & 1)) * row_bytes + vdg * 8;
-  int v_woff[4];
+  // operand reads: loop-invariant per-lane byte offsets inside one tile
+  int k_roff[KS];   // score operand A: key row kh*32 + r32, chunk 2*ks + hi
 #pragma unroll
-  for (int e = 0; e < 4; ++e) v_woff[e] = Lds<D>::K_BYTES + v_off(vdg * 4 + e, vkh);
-  // operand reads: loop-invariant per lane
-  int k_roff[KS];
+  for (int ks = 0; ks < KS; ++ks) k_roff[ks] = r32 * RB + (k_phys<D>(r32, 2 * ks + hi) << 4);
+  // value operand A via ds_read_b64_tr_b16: in each 16-lane group, lane 4a+c receives
+  // element c of the 8-byte pieces addressed by lanes a, a+4, a+8, a+12.  Lane j = 16g+a+4e
+  // therefore addresses key 16*kk + 4*(g>>1) + 8*half + e, value dims
+  // 32*vb + 16*(g&1) + 4*a .. +3, which hands lane l the transposed operand for value row
+  // 32*vb + (l & 31), keys 16*kk + 4*(l>>5) + {0,1,2,3} (half 0) and +8 (half 1): the key
+  // order of the score layout.
+  int v_roff[VB];
+  {
+    const int g = lane >> 4, a = lane & 3, e = (lane >> 2) & 3;
+    const int key = 4 * (g >> 1) + e;   // + 16*kk + 8*half: multiples of 4 (immediates)
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) k_roff[ks] = k_off<D>(r32, 2 * ks + hi);
-  int v_roff[4];
-#pragma unroll
-  for (int kk = 0; kk < 4; ++kk) v_roff[kk] = Lds<D>::K_BYTES + v_off(r32, 2 * kk + hi);
-
-  u32x4 kreg[KPT];
-  u32x2 vreg[8];
-
-  auto load_tile = [&](int kt) {
-    const int64_t t0 = (int64_t)kt * BK;
-    const int64_t bytes = ((int64_t)p.n_k - t0) * p.k_st * 2;
-    const __amdgpu_buffer_rsrc_t rk = make_rsrc(kg + t0 * p.k_st, bytes);
-    const __amdgpu_buffer_rsrc_t rv = make_rsrc(vg + t0 * p.k_st, bytes);
-#pragma unroll
-    for (int u = 0; u < KPT; ++u)
-      kreg[u] = __builtin_amdgcn_raw_buffer_load_b128(rk, k_goff, u * KROWS * row_bytes, 0);
-#pragma unroll
-    for (int q = 0; q < 8; ++q)
-      vreg[q] = __builtin_amdgcn_raw_buffer_load_b64(rv, v_goff, ((q & 3) + 8 * (q >> 2)) * row_bytes, 0);
-  };
-  auto store_tile = [&](auto bufc) {
-    constexpr int B = decltype(bufc)::value;
-    unsigned char* base = lds + B * BUF;
-#pragma unroll
-    for (int u = 0; u < KPT; ++u)
-      *reinterpret_cast<u32x4*>(base + k_woff + u * KROWS * D * 2) = kreg[u];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const unsigned sel = (e & 1) ? 0x07060302u : 0x05040100u;
-      u32x4 w;
-#pragma unroll
-      for (int m = 0; m < 4; ++m)
-        w[m] = __builtin_amdgcn_perm(vreg[2 * m + 1][e >> 1], vreg[2 * m][e >> 1], sel);
-      *reinterpret_cast<u32x4*>(base + v_woff[e]) = w;
+    for (int vb = 0; vb < VB; ++vb) {
+      const int dv = 32 * vb + 16 * (g & 1) + 4 * a;
+      v_roff[vb] = key * RB + (v_phys<D>(key, dv >> 3) << 4) + ((dv & 7) << 1);
     }
-  };
+  }
 
-  const float c2 = p.scale_log2;
-  unsigned long long my_pairs = 0;
-
-  // one key tile from LDS buffer B: scores, mask, online softmax, value product
-  auto compute_tile = [&](auto bufc, int kt) {
-    constexpr int B = decltype(bufc)::value;
-    const unsigned char* base = lds + B * BUF;
-
-    // S^T = K Q^T: lane holds keys 8*(j/4) + 4*hi + (j%4) (+32*kh) of query row r32
-    f32x16 sacc[2];
+  // S^T = K Q^T for the K tile in buffer B: lane holds keys 8*(j/4) + 4*hi + (j%4) (+32*kh)
+  // of query row r32
+  auto scores = [&](auto bufc, f32x16 (&sacc)[2]) {
+    const unsigned char* kt_base = ktile(bufc);
 #pragma unroll
     for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
@@ -247,11 +273,19 @@ void step_bf16_kernel(StepParams p) {
     for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
       for (int kh = 0; kh < 2; ++kh) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(base + k_roff[ks] + kh * 32 * D * 2);
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(kt_base + k_roff[ks] + kh * 32 * RB);
         sacc[kh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], sacc[kh], 0, 0, 0);
       }
     }
+  };
 
+  const float c2 = p.scale_log2;
+  unsigned long long my_pairs = 0;
+
+  // softmax of tile kt (scores in sacc) merged into the state, while the scores of tile
+  // kt+1 (K buffer KN) go onto the matrix cores; then O~ += V^T P^T from V buffer VBF
+  auto tile = [&](auto knext, auto vbuf, int kt, f32x16 (&sacc)[2], f32x16 (&snext)[2]) {
+    const unsigned char* vt_base = vtile(vbuf);
     // element mask on tiles that cross the diagonal or run past the block's end
     if ((kt >= kt_full) || ((kt + 1) * BK > p.n_k)) {
       const int lim = min(qrow + p.diag, p.n_k - 1) - kt * BK - 4 * hi;
@@ -296,6 +330,10 @@ void step_bf16_kernel(StepParams p) {
     }
     const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
 
+    // the next tile's scores: independent of everything below, so the matrix cores work
+    // on them while the vector unit forms this tile's probabilities
+    scores(knext, snext);
+
     // probabilities, rounded to bf16: the B operand of the value product; the row sum
     // adds the same rounded values (v_dot2 with ones), so the weights used for O~ and for
     // l agree exactly and a row with a single visible key normalises to exactly 1
@@ -324,36 +362,47 @@ void step_bf16_kernel(StepParams p) {
     }
     l_run += rs;
 
-    // O~^T += V^T P^T
+    // O~^T += V^T P^T; the transposed value operand comes from two transposing reads
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
 #pragma unroll
       for (int vb2 = 0; vb2 < VB; ++vb2) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(base + v_roff[kk] + vb2 * 32 * BK * 2);
+        const unsigned char* base = vt_base + v_roff[vb2] + kk * 16 * RB;
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base));
+        const s16x4 hi8 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + 8 * RB));
+        typedef short s16x8 __attribute__((ext_vector_type(8)));
+        const s16x8 both = __builtin_shufflevector(lo, hi8, 0, 1, 2, 3, 4, 5, 6, 7);
+        bf16x8 a;
+        __builtin_memcpy(&a, &both, sizeof a);
         oacc[vb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pk[kk], oacc[vb2], 0, 0, 0);
       }
     }
   };
 
-  // one pipeline step: prefetch tile kt+1 to registers, compute tile kt from buffer B,
-  // stage tile kt+1 into the other buffer, barrier.  The prefetch and the staging are
-  // unconditional (after the last live tile they fetch zeros or unused keys into the idle
-  // buffer): with no branch around them the loads are waited for only at the LDS stores,
-  // so the whole tile computation overlaps them.
-  auto step = [&](auto bufc, int kt) {
+  // One pipeline step for tile kt (B = kt & 1): K tile kt+1 is in K buffer 1-B, V tile kt
+  // in V buffer B.  Start the direct loads of K tile kt+2 into K buffer B and V tile kt+1
+  // into V buffer 1-B (both last read in the previous step), run the tile, wait for the
+  // loads, barrier.  The loads are unconditional: past the last live tile they fetch
+  // zeros or unused keys into buffers nobody reads.
+  f32x16 sa[2], sb[2];
+  auto step = [&](auto bufc, int kt, f32x16 (&scur)[2], f32x16 (&snext)[2]) {
     constexpr int B = decltype(bufc)::value;
-    load_tile(kt + 1);
-    compute_tile(bufc, kt);
-    store_tile(std::integral_constant<int, 1 - B>{});
+    load_k(bufc, kt + 2);
+    load_v(std::integral_constant<int, 1 - B>{}, kt + 1);
+    tile(std::integral_constant<int, 1 - B>{}, bufc, kt, scur, snext);
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's direct loads have landed
     __syncthreads();
   };
 
-  load_tile(0);
-  store_tile(std::integral_constant<int, 0>{});
+  load_k(std::integral_constant<int, 0>{}, 0);
+  load_v(std::integral_constant<int, 0>{}, 0);
+  load_k(std::integral_constant<int, 1>{}, 1);
+  __builtin_amdgcn_s_waitcnt(0x0F70);
   __syncthreads();
+  scores(std::integral_constant<int, 0>{}, sa);
   for (int kt = 0; kt < kt_live; kt += 2) {
-    step(std::integral_constant<int, 0>{}, kt);
-    if (kt + 1 < kt_live) step(std::integral_constant<int, 1>{}, kt + 1);
+    step(std::integral_constant<int, 0>{}, kt, sa, sb);
+    if (kt + 1 < kt_live) step(std::integral_constant<int, 1>{}, kt + 1, sb, sa);
   }
 
   // ---- write the state back ----------------------------------------------------------
@@ -381,6 +430,8 @@ void step_bf16_kernel(StepParams p) {
       atomicAdd(&p.dbg[2], dbg_acc);
     }
   }
+#undef ktile
+#undef vtile
 }
 
 template <int D>
