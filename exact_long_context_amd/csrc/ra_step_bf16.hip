@@ -14,19 +14,23 @@
 //    and keeps their q (as the MFMA B operand) and O~ (fp32 accumulators) in registers for
 //    the whole block.  Grid order is XCD-aware: workgroups that read the same KV head are
 //    dispatched to the same XCD, heaviest query tiles first.
-//  * Keys stream through LDS in 64-key tiles, double-buffered: the next tile's global loads
-//    (16-byte K rows, 8-byte V rows, all coalesced) are in flight while the current tile is
-//    on the matrix cores; one barrier per tile.
+//  * Keys stream through LDS in 64-key tiles, double-buffered, copied straight from HBM
+//    with buffer_load ... lds (no registers, no VALU): the next tiles' copies are in flight
+//    while the current tile is on the matrix cores; one barrier per tile.  K runs one tile
+//    ahead of V, so the scores of tile kt+1 overlap the probabilities of tile kt.
 //  * Scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16 (K from LDS
 //    as operand A, q from registers as operand B), so each lane ends up holding 16 keys of
-//    one query row: the row max and row sum need only in-lane work plus one
+//    one query row per 32 keys: the row max and row sum need only in-lane work plus one
 //    v_permlane32_swap with the partner lane.
 //  * The probabilities are rounded to bf16 in registers and reused directly as operand B of
-//    O~^T += V^T P^T.  V^T operand A comes from an LDS copy of V that is transposed (by
-//    v_perm_b32 in registers) on its way in, in the same permuted key order the score layout
-//    produces, so no data moves between lanes.
-//  * LDS rows are XOR-swizzled in 16-byte chunks so that both the staging writes and the
-//    operand reads hit distinct banks.
+//    O~^T += V^T P^T.  V stays untransposed in LDS; operand A is read with
+//    ds_read_b64_tr_b16, which transposes 16-bit elements within 16-lane groups and hands
+//    each lane the keys in the permuted order the score layout produces, so no data moves
+//    between lanes.
+//  * LDS rows are XOR-swizzled in 16-byte chunks for gfx950's 64 banks, so that both the
+//    direct copies and the operand reads hit distinct banks.
+//  * The running maximum may lag the true one by up to 2^8 in the terms; O~ and l are
+//    rescaled only when some row's maximum grew by more than that.
 //  * Causal skipping: the workgroup visits only the key tiles that hold an allowed pair
 //    and applies the element mask only on tiles that cross the diagonal or pass the
 //    block's end (ra_pos.h).
