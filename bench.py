@@ -100,6 +100,50 @@ def cpu_baseline(w, rank: int, q, k, v, seconds: float):
     }
 
 
+def hbm_passes(ra, q, k, v, ws, w, desc, reps: int = 20):
+    """The HBM-bound passes beside the lap: finalize over the lap's state, and block steps
+    with short KV blocks (the state read and write then outweigh the MFMA work).  Each is
+    timed with events on the current stream over `reps` launches; bytes are algorithmic."""
+    import torch
+    rows = w.batch * w.q_heads * w.n_local
+    d = w.head_dim
+    elem = q.element_size()
+    res = {}
+
+    def timed(fn):
+        fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    out = torch.empty((w.batch, w.q_heads, w.n_local, d), dtype=torch.float32, device=q.device)
+    lse = torch.empty((w.batch, w.q_heads, w.n_local), dtype=torch.float32, device=q.device)
+    # a state finalizes once: one resumed handle on the lap's state per launch, made beforehand
+    fin = [ra.RingState(q, k, w.P, workspace=ws, resume=True) for _ in range(reps + 1)]
+    it = iter(fin)
+    ms = timed(lambda: next(it).finalize(out, lse))
+    for f in fin:
+        f.close()
+    st = ra.RingState(q, k, w.P, workspace=ws, resume=True)
+    nbytes = rows * (4 * d + 8) + rows * (4 * d + 4)
+    res["finalize"] = {"ms": round(ms, 4), "bytes": nbytes, "GB_s": round(nbytes / ms / 1e6, 1),
+                       "frac_of_8TB_s": round(nbytes / ms / 1e6 / PEAK_HBM_GBS, 3)}
+    for nk in (256, 512, 1024):
+        kk, vv = k[:, :, :nk], v[:, :, :nk]
+        ms = timed(lambda: st.step(kk, vv, 0))
+        nbytes = 2 * rows * (4 * d + 8) + rows * d * elem + 2 * w.batch * w.kv_heads * nk * d * elem
+        flops = 4 * d * w.n_local * nk * w.q_heads * w.batch
+        res[f"step_nk{nk}"] = {"ms": round(ms, 4), "bytes": nbytes, "GB_s": round(nbytes / ms / 1e6, 1),
+                               "frac_of_8TB_s": round(nbytes / ms / 1e6 / PEAK_HBM_GBS, 3),
+                               "TFLOP_s": round(flops / ms / 1e9, 1)}
+    st.close()
+    return res
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -201,6 +245,8 @@ def main() -> int:
         "avg_launch_ms": round(avg_kernel_ms, 4),
     }
 
+    hbm = hbm_passes(ra, qd, kb[0], vb[0], ws, w, desc)
+
     cpu = None
     if not args.no_cpu_baseline:
         log("[bench] timing the oracle on host cores")
@@ -241,6 +287,7 @@ def main() -> int:
             "gpu": props.name, "cus": props.multi_processor_count,
             "torch": torch.__version__, "hip": torch.version.hip,
             "kernel_source_sha": kernel_source_sha(),
+            "hbm_passes": hbm,
         },
     }
     print(json.dumps(line), flush=True)
