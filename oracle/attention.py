@@ -25,7 +25,9 @@ state:
   slices ([P1] "Sharding the sequence, pinning the queries"; [P3] 位置编码必须使用
   全局位置, device p local index i -> global position p * N_local + i) or the
   round-robin striped layout, token t to rank t mod P (named as "striped" on
-  [P2] body and [P3] Causal section; the map itself is this project's reading).
+  [P2] body and [P3] Causal section; the map itself is this project's reading),
+  or the paired "zigzag" layout: 2P chunks of N/(2P) tokens, rank r holding
+  chunks r and 2P-1-r ([P1] "Striping the sequence to flatten the triangle").
 * The causal rule is on global positions: query q sees key k iff k <= q ([P3]
   Causal Attention 让环不再完全对称, and 位置编码必须使用全局位置).
 * ``tile_classes`` enumerates pairs per (query tile, key tile) and names a tile
@@ -81,6 +83,11 @@ def token_owner(N: int, P: int, layout: str) -> np.ndarray:
         return t // (N // P)
     if layout == "striped":
         return t % P
+    if layout == "zigzag":
+        if N % (2 * P):
+            raise ValueError("zigzag needs N to be a multiple of 2P")
+        chunk = t // (N // (2 * P))
+        return np.where(chunk < P, chunk, 2 * P - 1 - chunk)
     raise ValueError(f"unknown layout {layout!r}")
 
 

@@ -40,6 +40,11 @@ def _rel(a, b):
     return float(np.max(np.abs(a - b)) / max(np.max(np.abs(b)), 1e-300))
 
 
+def _golden_rows(name):
+    return [[int(x) for x in ln.split()] for ln in open(os.path.join(GOLDEN, name))
+            if ln.strip() and not ln.startswith("#")]
+
+
 def _blocks_for(k, v, N, P, layout):
     """Per-rank KV blocks with their global positions (from token ownership)."""
     out = []
@@ -90,8 +95,14 @@ def test_token_layouts():
         pos = oracle.tokens_of_rank(N, P, "striped", p)
         assert all(int(t) % P == p for t in pos)
         assert len(pos) == N // P
+    # zigzag: 2P chunks, rank p holds chunks p and 2P-1-p ([P1] "Striping the sequence to
+    # flatten the triangle"), written out in tests/golden/zigzag_chunks_p4.txt
+    table = _golden_rows("zigzag_chunks_p4.txt")
+    Nz, Pz = 16, 4
+    for p, *toks in table:
+        assert list(oracle.tokens_of_rank(Nz, Pz, "zigzag", p)) == toks
     # every token has exactly one owner
-    for layout in ("contiguous", "striped"):
+    for layout in ("contiguous", "striped", "zigzag"):
         allpos = np.concatenate([oracle.tokens_of_rank(N, P, layout, p) for p in range(P)])
         assert sorted(allpos.tolist()) == list(range(N))
 
@@ -163,7 +174,7 @@ def test_dense_rows_and_heads_subset():
 # The ring recipe (blockwise merge) against dense and against the unsharded sequence
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("layout", ["contiguous", "striped"])
+@pytest.mark.parametrize("layout", ["contiguous", "striped", "zigzag"])
 @pytest.mark.parametrize("P", [1, 2, 4, 8])
 @pytest.mark.parametrize("causal", [False, True])
 def test_blockwise_equals_dense(layout, P, causal):
@@ -184,7 +195,7 @@ def test_blockwise_equals_dense(layout, P, causal):
         assert np.max(np.abs(lse_ring[fin] - lse_ref[fin])) <= 1e-12
 
 
-@pytest.mark.parametrize("layout", ["contiguous", "striped"])
+@pytest.mark.parametrize("layout", ["contiguous", "striped", "zigzag"])
 @pytest.mark.parametrize("P", [2, 4])
 def test_whole_ring_equals_unsharded_causal_sdpa(layout, P):
     """Reassemble every rank's lap; it must equal causal attention on the full sequence.
@@ -424,6 +435,44 @@ def test_live_pair_closed_forms_at_full_size(name, N, P, r, layout, per_head):
         assert c == expect
         total += c
     assert total == per_head
+
+
+def test_zigzag_balances_the_causal_work():
+    """[P1] "Striping the sequence to flatten the triangle": every rank gets one early and
+    one late chunk, so the causal work is shared evenly.  Closed form: queries in chunk i
+    (c tokens) see i*c^2 + c(c+1)/2 keys in all, so rank r, holding chunks r and 2P-1-r,
+    sees (2P-1)c^2 + c^2 + c = 2P c^2 + c, the same for every rank; per block, a chunk pair
+    (query chunk a, key chunk b) holds c^2 pairs when b < a, c(c+1)/2 when b == a, else 0."""
+    N, P = 131072, 8
+    c = N // (2 * P)
+    for r in range(P):
+        qp = oracle.tokens_of_rank(N, P, "zigzag", r)
+        total = 0
+        for j in range(P):
+            kp = oracle.tokens_of_rank(N, P, "zigzag", j)
+            got = oracle.live_pair_count(qp, kp, True)
+            expect = 0
+            for a in (r, 2 * P - 1 - r):
+                for b in (j, 2 * P - 1 - j):
+                    expect += c * c if b < a else (c * (c + 1) // 2 if b == a else 0)
+            assert got == expect
+            total += got
+        assert total == 2 * P * c * c + c == 1_073_750_016
+    # the contiguous ramp it replaces: rank 0 and rank 7 differ fifteen-fold
+    n = N // P
+    ramp = [oracle.live_pair_count(oracle.tokens_of_rank(N, P, "contiguous", r), np.arange(N), True)
+            for r in (0, P - 1)]
+    assert ramp == [n * (n + 1) // 2, (P - 1) * n * n + n * (n + 1) // 2]
+
+
+def test_zigzag_pair_counts_match_brute_force():
+    for P in (1, 2, 3, 4):
+        N = 2 * P * 6
+        for r in range(P):
+            qp = oracle.tokens_of_rank(N, P, "zigzag", r)
+            for j in range(P):
+                kp = oracle.tokens_of_rank(N, P, "zigzag", j)
+                assert oracle.live_pair_count(qp, kp, True) == oracle.brute_force_pair_count(qp, kp, True)
 
 
 def _brute_tile_classes(qp, kp, tq, tk):
