@@ -31,7 +31,7 @@ if ROOT not in sys.path:
 PEAK_BF16_TFLOPS = 2516.6   # 256 CU x 2.4 GHz x 4096 dense bf16 flop/clk/CU (MI355X)
 PEAK_HBM_GBS = 8000.0
 DEFAULT_WORKLOAD = "noncausal_n131072_p8_h32"
-MASK_CODE = {"none": 0, "causal_contiguous": 1, "causal_striped": 2}
+MASK_CODE = {"none": 0, "causal_contiguous": 1, "causal_striped": 2, "causal_zigzag": 3}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "step_bf16_traffic.txt")
 STEP_SOURCE = os.path.join(ROOT, "exact_long_context_amd", "csrc", "ra_step_bf16.hip")
 

@@ -22,6 +22,7 @@ from ._abi import (  # noqa: F401
     RA_E_UNSUPPORTED,
     RA_MASK_CAUSAL_CONTIGUOUS,
     RA_MASK_CAUSAL_STRIPED,
+    RA_MASK_CAUSAL_ZIGZAG,
     RA_MASK_NONE,
     RA_OK,
     RA_TILE_EMPTY,
@@ -42,6 +43,7 @@ MASKS = {
     "none": RA_MASK_NONE,
     "causal_contiguous": RA_MASK_CAUSAL_CONTIGUOUS,
     "causal_striped": RA_MASK_CAUSAL_STRIPED,
+    "causal_zigzag": RA_MASK_CAUSAL_ZIGZAG,
 }
 
 
@@ -109,8 +111,13 @@ def plan_block(desc: ra_desc, kv_len: int, mask_kind: int, q_offset: int = 0,
 def tile_classes(desc: ra_desc, kv_len: int, mask_kind: int, q_offset: int = 0,
                  k_offset: int = 0) -> np.ndarray:
     s = plan_block(desc, kv_len, mask_kind, q_offset, k_offset)
-    nqt = -(-desc.q_len // s["tile_q"])
-    nkt = -(-kv_len // s["tile_k"])
+    if mask_kind == RA_MASK_CAUSAL_ZIGZAG:   # tiles follow the two chunks on each axis
+        c = desc.q_len // 2
+        nqt = 2 * -(-c // s["tile_q"])
+        nkt = 2 * -(-c // s["tile_k"])
+    else:
+        nqt = -(-desc.q_len // s["tile_q"])
+        nkt = -(-kv_len // s["tile_k"])
     out = np.zeros((nqt, nkt), dtype=np.uint8)
     check(lib().ra_tile_classes(C.byref(desc), kv_len, mask_kind, q_offset, k_offset,
                                 out.ctypes.data_as(C.c_void_p), out.nbytes))
@@ -200,7 +207,7 @@ def block_offsets(mask_kind: int, rank: int, block: int, q_len: int, kv_len: int
     """(q_offset, k_offset) of a block under a mask's layout (include/ra.h conventions)."""
     if mask_kind == RA_MASK_CAUSAL_CONTIGUOUS:
         return rank * q_len, block * kv_len
-    if mask_kind == RA_MASK_CAUSAL_STRIPED:
+    if mask_kind in (RA_MASK_CAUSAL_STRIPED, RA_MASK_CAUSAL_ZIGZAG):
         return rank, block
     return 0, 0
 

@@ -22,6 +22,7 @@ RA_E_HIP = -4
 RA_MASK_NONE = 0
 RA_MASK_CAUSAL_CONTIGUOUS = 1
 RA_MASK_CAUSAL_STRIPED = 2
+RA_MASK_CAUSAL_ZIGZAG = 3
 
 RA_DTYPE_BF16 = 0
 RA_DTYPE_F32 = 1

@@ -103,36 +103,85 @@ int32_t pos_stride(int32_t mask_kind, const ra_desc* d) {
   return mask_kind == RA_MASK_CAUSAL_STRIPED ? d->ring_size : 1;
 }
 
+// A block as launches see it: rows [row0, row0 + rows) of the state against keys
+// [key0, key0 + keys) of the block, with every position fact folded into diag.  The
+// single-range layouts give one sub-block.  The zigzag layout ("GPU ring attention",
+// section "Striping the sequence to flatten the triangle": 2P chunks, rank r holds chunks
+// r and 2P-1-r) gives four, one per (query chunk, key chunk): each is a contiguous causal
+// block with its own diagonal, and a chunk pair wholly in the future is empty.
+struct Sub {
+  int32_t row0, rows, key0, keys, diag;
+  int64_t pairs;   // allowed (row, key) pairs of one head
+};
+
+int64_t pairs_of(int32_t rows, int32_t keys, int32_t diag) {
+  int64_t n = 0;
+  for (int32_t i = 0; i < rows; ++i) n += ra::keys_visible(i, diag, keys);
+  return n;
+}
+
+int subs_of(const ra_desc* d, int32_t kv_len, int32_t mask_kind, int64_t q_off, int64_t k_off,
+            Sub* out, int* n_out) {
+  if (kv_len < 0) return fail(RA_E_INVALID, "kv_len must be >= 0");
+  if (mask_kind < RA_MASK_NONE || mask_kind > RA_MASK_CAUSAL_ZIGZAG)
+    return fail(RA_E_INVALID, "unknown mask_kind %d", mask_kind);
+  if (mask_kind != RA_MASK_CAUSAL_ZIGZAG) {
+    const int causal = mask_kind != RA_MASK_NONE;
+    const int32_t diag = ra::diag_shift(causal, q_off, k_off, pos_stride(mask_kind, d), d->q_len, kv_len);
+    out[0] = Sub{0, d->q_len, 0, kv_len, diag, pairs_of(d->q_len, kv_len, diag)};
+    *n_out = 1;
+    return RA_OK;
+  }
+  const int64_t P = d->ring_size;
+  if (d->q_len % 2 != 0) return fail(RA_E_INVALID, "zigzag: q_len %d is not two chunks", d->q_len);
+  if (kv_len != d->q_len)
+    return fail(RA_E_INVALID, "zigzag: kv_len %d must equal q_len %d (one chunk length)", kv_len, d->q_len);
+  if (q_off < 0 || q_off >= P || k_off < 0 || k_off >= P)
+    return fail(RA_E_INVALID, "zigzag: q_offset and k_offset are ranks in [0, %lld)", (long long)P);
+  const int32_t c = d->q_len / 2;
+  const int64_t q_chunk[2] = {q_off, 2 * P - 1 - q_off};
+  const int64_t k_chunk[2] = {k_off, 2 * P - 1 - k_off};
+  for (int qa = 0; qa < 2; ++qa)
+    for (int ka = 0; ka < 2; ++ka) {
+      const int32_t diag = ra::diag_shift(1, q_chunk[qa] * c, k_chunk[ka] * c, 1, c, c);
+      out[2 * qa + ka] = Sub{qa * c, c, ka * c, c, diag, pairs_of(c, c, diag)};
+    }
+  *n_out = 4;
+  return RA_OK;
+}
+
 // Plan one block: counts for the whole launch (all batches and query heads).
 int plan(const ra_desc* d, int32_t kv_len, int32_t mask_kind, int64_t q_off, int64_t k_off,
-         ra_stats* out, int32_t* diag_out) {
-  if (kv_len < 0) return fail(RA_E_INVALID, "kv_len must be >= 0");
-  if (mask_kind < RA_MASK_NONE || mask_kind > RA_MASK_CAUSAL_STRIPED)
-    return fail(RA_E_INVALID, "unknown mask_kind %d", mask_kind);
-  const int causal = mask_kind != RA_MASK_NONE;
-  const int32_t s = pos_stride(mask_kind, d);
-  const int32_t diag = ra::diag_shift(causal, q_off, k_off, s, d->q_len, kv_len);
+         ra_stats* out, Sub* subs, int* n_subs) {
+  Sub local[4];
+  int n_local = 0;
+  if (!subs) subs = local;
+  if (!n_subs) n_subs = &n_local;
+  int rc = subs_of(d, kv_len, mask_kind, q_off, k_off, subs, n_subs);
+  if (rc) return rc;
   const int tq = tile_q_of(d), tk = tile_k_of(d);
   std::memset(out, 0, sizeof *out);
   out->tile_q = tq;
   out->tile_k = tk;
   const int64_t heads = (int64_t)d->batch * d->q_heads;
-  int64_t pairs = 0;
-  for (int32_t i = 0; i < d->q_len; ++i) pairs += ra::keys_visible(i, diag, kv_len);
-  int64_t full = 0, live = 0;
-  const int32_t n_qt = (d->q_len + tq - 1) / tq;
-  const int32_t n_kt = (kv_len + tk - 1) / tk;
-  for (int32_t a = 0; a < n_qt; ++a) {
-    const int32_t i0 = a * tq, i1 = i0 + tq < d->q_len ? i0 + tq : d->q_len;
-    full += ra::tiles_full(i0, i1, diag, kv_len, tk);
-    live += ra::tiles_live(i0, i1, diag, kv_len, tk);
+  int64_t pairs = 0, full = 0, live = 0, tiles = 0;
+  for (int u = 0; u < *n_subs; ++u) {
+    const Sub& b = subs[u];
+    pairs += b.pairs;
+    const int32_t n_qt = (b.rows + tq - 1) / tq;
+    const int32_t n_kt = (b.keys + tk - 1) / tk;
+    tiles += (int64_t)n_qt * n_kt;
+    for (int32_t a = 0; a < n_qt; ++a) {
+      const int32_t i0 = a * tq, i1 = i0 + tq < b.rows ? i0 + tq : b.rows;
+      full += ra::tiles_full(i0, i1, b.diag, b.keys, tk);
+      live += ra::tiles_live(i0, i1, b.diag, b.keys, tk);
+    }
   }
   out->live_pairs = pairs * heads;
   out->tiles_full = full * heads;
   out->tiles_partial = (live - full) * heads;
-  out->tiles_empty = ((int64_t)n_qt * n_kt - live) * heads;
+  out->tiles_empty = (tiles - live) * heads;
   if (pairs > 0) out->blocks_run = 1; else out->blocks_skipped = 1;
-  if (diag_out) *diag_out = diag;
   return RA_OK;
 }
 
@@ -210,8 +259,9 @@ int ra_block_step(ra_state* st, const void* k, const void* v, int32_t kv_len, in
   if (st->finalized) return fail(RA_E_STATE, "step after finalize");
   const ra_desc* d = &st->desc;
   ra_stats s;
-  int32_t diag = 0;
-  int rc = plan(d, kv_len, mask_kind, q_offset, k_offset, &s, &diag);
+  Sub subs[4];
+  int n_subs = 0;
+  int rc = plan(d, kv_len, mask_kind, q_offset, k_offset, &s, subs, &n_subs);
   if (rc) return rc;
   if (kv_len > 0) {
     if (!k || !v) return fail(RA_E_INVALID, "K_j or V_j is NULL");
@@ -223,33 +273,58 @@ int ra_block_step(ra_state* st, const void* k, const void* v, int32_t kv_len, in
     add_stats(&st->stats, &s);
     return RA_OK;
   }
-  ra::StepParams p;
-  p.q = st->q;
-  p.k = k;
-  p.v = v;
-  p.o_acc = st->o_acc;
-  p.m = st->m;
-  p.l = st->l;
-  p.q_sb = d->q_strides[0];
-  p.q_sh = d->q_strides[1];
-  p.q_st = d->q_strides[2];
-  p.k_sb = d->kv_strides[0];
-  p.k_sh = d->kv_strides[1];
-  p.k_st = d->kv_strides[2];
-  p.batch = d->batch;
-  p.q_heads = d->q_heads;
-  p.kv_heads = d->kv_heads;
-  p.group = d->q_heads / d->kv_heads;
-  p.n_q = d->q_len;
-  p.n_k = kv_len;
-  p.diag = diag;
-  p.scale_log2 = d->softmax_scale * 1.4426950408889634f;
-  p.fresh = st->fresh;
-  p.dbg = st->dbg;
+  const size_t elem = d->dtype == RA_DTYPE_BF16 ? 2 : 4;
   hipStream_t stream = static_cast<hipStream_t>(d->stream);
-  hipError_t e = d->dtype == RA_DTYPE_BF16 ? ra::launch_step_bf16(p, d->head_dim, stream)
-                                           : ra::launch_step_f32(p, d->head_dim, stream);
-  if (e != hipSuccess) return hip_fail(e, "step kernel launch");
+  auto launch = [&](const Sub& b, int fresh) -> int {
+    ra::StepParams p;
+    p.q = static_cast<const char*>(st->q) + (int64_t)b.row0 * d->q_strides[2] * elem;
+    p.k = static_cast<const char*>(k) + (int64_t)b.key0 * d->kv_strides[2] * elem;
+    p.v = static_cast<const char*>(v) + (int64_t)b.key0 * d->kv_strides[2] * elem;
+    p.o_acc = st->o_acc + (int64_t)b.row0 * d->head_dim;
+    p.m = st->m + b.row0;
+    p.l = st->l + b.row0;
+    p.q_sb = d->q_strides[0];
+    p.q_sh = d->q_strides[1];
+    p.q_st = d->q_strides[2];
+    p.k_sb = d->kv_strides[0];
+    p.k_sh = d->kv_strides[1];
+    p.k_st = d->kv_strides[2];
+    p.batch = d->batch;
+    p.q_heads = d->q_heads;
+    p.kv_heads = d->kv_heads;
+    p.group = d->q_heads / d->kv_heads;
+    p.n_q = b.rows;
+    p.n_k = b.keys;
+    p.state_rows = d->q_len;
+    p.diag = b.diag;
+    p.scale_log2 = d->softmax_scale * 1.4426950408889634f;
+    p.fresh = fresh;
+    p.dbg = st->dbg;
+    hipError_t e = d->dtype == RA_DTYPE_BF16 ? ra::launch_step_bf16(p, d->head_dim, stream)
+                                             : ra::launch_step_f32(p, d->head_dim, stream);
+    if (e != hipSuccess) return hip_fail(e, "step kernel launch");
+    return RA_OK;
+  };
+  // Sub-blocks that share query rows run in order on the stream.  Only the first launch
+  // that touches a row range of a fresh state starts from the empty state; a fresh row
+  // range with no allowed pair in this block still gets the empty state written (with no
+  // keys), because the state stops being fresh as a whole.
+  const int per_rows = n_subs == 4 ? 2 : 1;
+  for (int g = 0; g < n_subs; g += per_rows) {
+    bool launched = false;
+    for (int u = g; u < g + per_rows; ++u) {
+      if (subs[u].pairs == 0) continue;
+      rc = launch(subs[u], st->fresh && !launched);
+      if (rc) return rc;
+      launched = true;
+    }
+    if (!launched && st->fresh) {
+      Sub empty = subs[g];
+      empty.keys = 0;
+      rc = launch(empty, 1);
+      if (rc) return rc;
+    }
+  }
   st->fresh = 0;
   add_stats(&st->stats, &s);
   return RA_OK;
@@ -299,7 +374,7 @@ int ra_plan_block(const ra_desc* desc, int32_t kv_len, int32_t mask_kind, int64_
   int rc = check_desc(desc);
   if (rc) return rc;
   if (!out) return fail(RA_E_INVALID, "out is NULL");
-  return plan(desc, kv_len, mask_kind, q_offset, k_offset, out, nullptr);
+  return plan(desc, kv_len, mask_kind, q_offset, k_offset, out, nullptr, nullptr);
 }
 
 int ra_tile_classes(const ra_desc* desc, int32_t kv_len, int32_t mask_kind, int64_t q_offset,
@@ -307,22 +382,31 @@ int ra_tile_classes(const ra_desc* desc, int32_t kv_len, int32_t mask_kind, int6
   int rc = check_desc(desc);
   if (rc) return rc;
   ra_stats s;
-  int32_t diag = 0;
-  rc = plan(desc, kv_len, mask_kind, q_offset, k_offset, &s, &diag);
+  Sub subs[4];
+  int n_subs = 0;
+  rc = plan(desc, kv_len, mask_kind, q_offset, k_offset, &s, subs, &n_subs);
   if (rc) return rc;
   const int tq = tile_q_of(desc), tk = tile_k_of(desc);
-  const int32_t n_qt = (desc->q_len + tq - 1) / tq;
-  const int32_t n_kt = (kv_len + tk - 1) / tk;
-  if ((size_t)n_qt * n_kt > cap) return fail(RA_E_INVALID, "host_out holds %zu bytes, need %lld", cap,
-                                             (long long)n_qt * n_kt);
-  if (n_qt * (int64_t)n_kt > 0 && !host_out) return fail(RA_E_INVALID, "host_out is NULL");
-  for (int32_t a = 0; a < n_qt; ++a) {
-    const int32_t i0 = a * tq, i1 = i0 + tq < desc->q_len ? i0 + tq : desc->q_len;
-    for (int32_t c = 0; c < n_kt; ++c) {
-      const int32_t t0 = c * tk, t1 = t0 + tk < kv_len ? t0 + tk : kv_len;
-      host_out[(size_t)a * n_kt + c] = (uint8_t)ra::classify_tile(i0, i1, t0, t1, diag);
+  // tile grid: per query chunk and key chunk (one of each for the single-range layouts)
+  const int n_side = n_subs == 4 ? 2 : 1;
+  const int32_t qt_c = (subs[0].rows + tq - 1) / tq;
+  const int32_t kt_c = (subs[0].keys + tk - 1) / tk;
+  const int64_t n_qt = (int64_t)n_side * qt_c, n_kt = (int64_t)n_side * kt_c;
+  if ((size_t)(n_qt * n_kt) > cap)
+    return fail(RA_E_INVALID, "host_out holds %zu bytes, need %lld", cap, (long long)(n_qt * n_kt));
+  if (n_qt * n_kt > 0 && !host_out) return fail(RA_E_INVALID, "host_out is NULL");
+  for (int qa = 0; qa < n_side; ++qa)
+    for (int ka = 0; ka < n_side; ++ka) {
+      const Sub& b = subs[qa * n_side + ka];
+      for (int32_t a = 0; a < qt_c; ++a) {
+        const int32_t i0 = a * tq, i1 = i0 + tq < b.rows ? i0 + tq : b.rows;
+        for (int32_t c = 0; c < kt_c; ++c) {
+          const int32_t t0 = c * tk, t1 = t0 + tk < b.keys ? t0 + tk : b.keys;
+          host_out[(size_t)(qa * qt_c + a) * n_kt + ka * kt_c + c] =
+              (uint8_t)ra::classify_tile(i0, i1, t0, t1, b.diag);
+        }
+      }
     }
-  }
   return RA_OK;
 }
 

@@ -7,7 +7,9 @@
 namespace ra {
 
 // Everything one step launch needs.  Strides are in elements; the head dimension is
-// contiguous.  All position logic is already folded into `diag` (see ra_pos.h).
+// contiguous.  All position logic is already folded into `diag` (see ra_pos.h).  A launch
+// covers rows [0, n_q) and keys [0, n_k) of what q, k, v, o_acc, m and l point at, which may
+// be a sub-range of the state (the zigzag layout runs one launch per pair of chunks).
 struct StepParams {
   const void* q;
   const void* k;
@@ -18,7 +20,9 @@ struct StepParams {
   int64_t q_sb, q_sh, q_st;
   int64_t k_sb, k_sh, k_st;
   int32_t batch, q_heads, kv_heads, group;  // group = q_heads / kv_heads
-  int32_t n_q, n_k;
+  int32_t n_q, n_k;     // query rows and keys of this launch
+  int32_t state_rows;   // rows per (batch, head) in the state (>= n_q; the state pointers
+                        // and q already point at this launch's first row)
   int32_t diag;        // key t is visible to row i iff t <= i + diag
   float scale_log2;    // softmax scale * log2(e)
   int32_t fresh;       // 1: the state has never been written; start from the empty state

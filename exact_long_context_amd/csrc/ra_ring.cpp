@@ -113,7 +113,7 @@ extern "C" int ra_ring_lap_emulated(const ra_desc* desc, const void* q, void* wo
     if (lap->mask_kind == RA_MASK_CAUSAL_CONTIGUOUS) {
       q_off = (int64_t)r * desc->q_len;
       k_off = (int64_t)j * lap->kv_len;
-    } else if (lap->mask_kind == RA_MASK_CAUSAL_STRIPED) {
+    } else if (lap->mask_kind == RA_MASK_CAUSAL_STRIPED || lap->mask_kind == RA_MASK_CAUSAL_ZIGZAG) {
       q_off = r;
       k_off = j;
     }

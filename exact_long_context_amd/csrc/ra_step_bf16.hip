@@ -161,7 +161,7 @@ void step_bf16_kernel(StepParams p) {
 
   const int qrow = i0 + wave * WROWS + r32;
   const bool row_ok = qrow < p.n_q;
-  const int64_t srow = ((int64_t)b * p.q_heads + h) * p.n_q + qrow;
+  const int64_t srow = ((int64_t)b * p.q_heads + h) * p.state_rows + qrow;
 
   if (DEBUG && tid == 0) dbg_acc = 0;
 

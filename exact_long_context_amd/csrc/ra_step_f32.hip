@@ -47,7 +47,7 @@ __global__ __launch_bounds__(NT) void step_f32_kernel(StepParams p) {
   const int i1 = min(i0 + TQ, p.n_q);
   const int i = i0 + row;
   const bool row_ok = i < p.n_q;
-  const int64_t srow = ((int64_t)b * p.q_heads + h) * p.n_q + i;   // state row index
+  const int64_t srow = ((int64_t)b * p.q_heads + h) * p.state_rows + i;   // state row index
 
   const int kt_live = tiles_live(i0, i1, p.diag, p.n_k, TK);
   const int kt_full = tiles_full(i0, i1, p.diag, p.n_k, TK);

@@ -1,8 +1,9 @@
 """Device-side data placement for the emulated ring (torch plumbing only).
 
 Cuts global K/V [B, Hkv, N, d] into the P per-rank blocks a ring would hold:
-contiguous slices (rank j owns tokens j*N/P .. (j+1)*N/P - 1) or the striped
-round-robin layout (rank j owns tokens t with t mod P == j), each block made
+contiguous slices (rank j owns tokens j*N/P .. (j+1)*N/P - 1), the striped
+round-robin layout (rank j owns tokens t with t mod P == j) or the zigzag layout
+(rank j owns chunks j and 2P-1-j of 2P, in that order), each block made
 contiguous [B, Hkv, N/P, d] so it can be moved with one copy.  The positions of
 those tokens are not materialised: the library derives them from the block
 index (include/ra.h).
@@ -24,6 +25,14 @@ def shard_blocks(k_global, v_global, P: int, layout: str):
         elif layout == "striped":
             ks.append(k_global[:, :, j::P].contiguous())
             vs.append(v_global[:, :, j::P].contiguous())
+        elif layout == "zigzag":
+            import torch
+            c = n // 2
+            if n % 2:
+                raise ValueError("zigzag needs N to be a multiple of 2P")
+            lo, hi = j * c, (2 * P - 1 - j) * c
+            ks.append(torch.cat([k_global[:, :, lo:lo + c], k_global[:, :, hi:hi + c]], dim=2).contiguous())
+            vs.append(torch.cat([v_global[:, :, lo:lo + c], v_global[:, :, hi:hi + c]], dim=2).contiguous())
         else:
             raise ValueError(layout)
     return ks, vs

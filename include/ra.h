@@ -25,6 +25,14 @@
  * layout rank r passes q_offset = r * q_len and block j k_offset = j * kv_len; for the
  * striped layout q_offset = r and k_offset = j.  Offsets are ignored for RA_MASK_NONE.
  *
+ * RA_MASK_CAUSAL_ZIGZAG is the paired layout of "GPU ring attention", section "Striping
+ * the sequence to flatten the triangle": the sequence is cut into 2P chunks of c tokens
+ * and rank r holds chunk r followed by chunk 2P-1-r, so local row i < c sits at position
+ * r*c + i and row c + i at (2P-1-r)*c + i; a KV block from rank j is laid out the same
+ * way.  Then q_len = kv_len = 2c, q_offset = r and k_offset = j (ranks in [0, P), P =
+ * desc.ring_size).  A step runs as up to four contiguous causal sub-blocks (query chunk x
+ * key chunk); a chunk pair wholly in the future is skipped like an empty block.
+ *
  * Fully masked work is skipped at two granularities ("GPU ring attention", section
  * "Striping the sequence to flatten the triangle"; charlestar page, Causal section,
  * strictly-future / diagonal-crossing / unmasked rule): a block with no allowed pair
@@ -66,7 +74,8 @@ extern "C" {
 typedef enum {
   RA_MASK_NONE = 0,               /* every key of every block is allowed */
   RA_MASK_CAUSAL_CONTIGUOUS = 1,  /* k <= q, positions offset + index (stride 1) */
-  RA_MASK_CAUSAL_STRIPED = 2      /* k <= q, positions offset + index * ring_size */
+  RA_MASK_CAUSAL_STRIPED = 2,     /* k <= q, positions offset + index * ring_size */
+  RA_MASK_CAUSAL_ZIGZAG = 3       /* k <= q, rank r holds chunks r and 2P-1-r of 2P */
 } ra_mask_kind;
 
 typedef enum {
@@ -174,7 +183,9 @@ int ra_plan_block(const ra_desc* desc, int32_t kv_len, int32_t mask_kind,
 
 /* Class of every (query tile, key tile) of one head for this block, row-major
  * [ceil(q_len/tile_q)][ceil(kv_len/tile_k)] into host memory host_out of cap bytes,
- * using the kernel's own tile sizes (reported by ra_plan_block). */
+ * using the kernel's own tile sizes (reported by ra_plan_block).  For
+ * RA_MASK_CAUSAL_ZIGZAG the tiles follow the chunks: [2*ceil(c/tile_q)][2*ceil(c/tile_k)]
+ * with c = q_len / 2, the first half of each axis covering the first chunk. */
 int ra_tile_classes(const ra_desc* desc, int32_t kv_len, int32_t mask_kind,
                     int64_t q_offset, int64_t k_offset, uint8_t* host_out, size_t cap);
 
@@ -189,9 +200,10 @@ int ra_tile_classes(const ra_desc* desc, int32_t kv_len, int32_t mask_kind,
  * copy-after-consume and compute-after-arrival ("GPU ring attention", section "Hiding the
  * ring behind the GEMMs"; charlestar page, section 双缓冲是重叠成立的基础).
  * recv_k[2], recv_v[2] are the receive buffers (block_bytes each).  Positions follow
- * mask_kind (contiguous: rank * q_len and j * kv_len; striped: rank and j).  Writes O
- * and lse as ra_finalize does; stats_out (host, may be NULL) receives the lap's counts.
- * The workspace is used as the state.  Events are created and destroyed per call. */
+ * mask_kind (contiguous: rank * q_len and j * kv_len; striped and zigzag: rank and j).
+ * Writes O and lse as ra_finalize does; stats_out (host, may be NULL) receives the lap's
+ * counts.  The workspace is used as the state.  Events are created and destroyed per
+ * call. */
 typedef struct ra_lap {
   const void* const* k_blocks;  /* host array [P] of device pointers */
   const void* const* v_blocks;  /* host array [P] of device pointers */

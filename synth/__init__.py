@@ -45,7 +45,7 @@ class Workload:
     kv_heads: int
     head_dim: int
     dtype: str                 # "bf16" or "f32"
-    mask: str                  # "none", "causal_contiguous", "causal_striped"
+    mask: str                  # "none", "causal_contiguous", "causal_striped", "causal_zigzag"
     ranks: tuple               # ranks measured / checked
     value_scale: float = 1.0   # inputs multiplied by this before rounding
     seed: int = 0
@@ -58,7 +58,7 @@ class Workload:
 
     @property
     def layout(self) -> str:
-        return "striped" if self.mask == "causal_striped" else "contiguous"
+        return {"causal_striped": "striped", "causal_zigzag": "zigzag"}.get(self.mask, "contiguous")
 
 
 WORKLOADS = {
@@ -72,6 +72,10 @@ WORKLOADS = {
     "causal_contig_n131072_p8_h32": Workload("causal_contig_n131072_p8_h32", 131072, 8, 1, 32, 32,
                                              128, "bf16", "causal_contiguous", (0, 7),
                                              value_scale=1 / math.sqrt(128)),
+    # Causal zigzag: the non-causal tensors' shapes, rank r holding chunks r and 15 - r of 16;
+    # the first and the last rank (equal work, unlike the contiguous ramp).
+    "zigzag_n131072_p8_h32": Workload("zigzag_n131072_p8_h32", 131072, 8, 1, 32, 32, 128, "bf16",
+                                      "causal_zigzag", (0, 7), value_scale=1 / math.sqrt(128)),
     # Causal striped: N=262144, P=16, token t on rank t mod 16, rank 5.
     "striped_n262144_p16_h32": Workload("striped_n262144_p16_h32", 262144, 16, 1, 32, 32, 128,
                                         "bf16", "causal_striped", (5,)),

@@ -11,7 +11,7 @@ import torch
 import oracle
 import synth
 
-LAYOUT_OF_MASK = {0: "contiguous", 1: "contiguous", 2: "striped"}
+LAYOUT_OF_MASK = {0: "contiguous", 1: "contiguous", 2: "striped", 3: "zigzag"}
 
 # bf16 inputs with fp32 accumulation, against the fp64 oracle on the same bf16 values
 BF16_MAX_ABS = 2e-2

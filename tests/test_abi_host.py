@@ -80,6 +80,61 @@ def test_tile_classes_match_oracle(dtype, layout, mask):
                 assert st["blocks_skipped"] == int(st["live_pairs"] == 0)
 
 
+def _zigzag_tile_classes(N, P, r, j, tq, tk):
+    """The oracle's classes per (query chunk, key chunk), assembled on the chunk tiling."""
+    qp = oracle.tokens_of_rank(N, P, "zigzag", r)
+    kp = oracle.tokens_of_rank(N, P, "zigzag", j)
+    c = qp.size // 2
+    rows = []
+    for qa in range(2):
+        rows.append(np.concatenate([oracle.tile_classes(qp[qa * c:(qa + 1) * c], kp[ka * c:(ka + 1) * c],
+                                                        tq, tk, True) for ka in range(2)], axis=1))
+    return np.concatenate(rows, axis=0), qp, kp
+
+
+@pytest.mark.parametrize("dtype", [ra.RA_DTYPE_BF16, ra.RA_DTYPE_F32])
+def test_zigzag_tile_classes_and_counts_match_oracle(dtype):
+    for P, N in ((1, 512), (2, 1200), (3, 1536), (4, 4096), (8, 4 * 8 * 300)):
+        n = N // P
+        d = _desc(q_len=n, dtype=dtype, P=P)
+        for r in sorted({0, P // 2, P - 1}):
+            for j in range(P):
+                st = ra.plan_block(d, n, ra.RA_MASK_CAUSAL_ZIGZAG, r, j)
+                got = ra.tile_classes(d, n, ra.RA_MASK_CAUSAL_ZIGZAG, r, j)
+                want, qp, kp = _zigzag_tile_classes(N, P, r, j, st["tile_q"], st["tile_k"])
+                assert np.array_equal(got, want), (P, r, j)
+                heads = d.batch * d.q_heads
+                assert st["live_pairs"] == heads * oracle.live_pair_count(qp, kp, True)
+                assert st["tiles_full"] == heads * int((want == oracle.FULL).sum())
+                assert st["tiles_partial"] == heads * int((want == oracle.PARTIAL).sum())
+                assert st["tiles_empty"] == heads * int((want == oracle.EMPTY).sum())
+                assert st["blocks_skipped"] == int(st["live_pairs"] == 0)
+
+
+def test_zigzag_full_size_ranks_do_equal_work():
+    # the 131072-token, 8-rank ring: every rank's lap holds 2P c^2 + c pairs per head
+    N, P, Hq = 131072, 8, 32
+    n, c = N // P, N // (2 * P)
+    d = _desc(q_len=n, q_heads=Hq, kv_heads=Hq, P=P)
+    for r in range(P):
+        total = sum(ra.plan_block(d, n, ra.RA_MASK_CAUSAL_ZIGZAG, r, j)["live_pairs"] for j in range(P))
+        assert total == Hq * (2 * P * c * c + c)
+
+
+def test_zigzag_argument_validation():
+    lib = ra.lib()
+    s = ra.ra_stats()
+    d = _desc(q_len=64, P=4)
+    Z = ra.RA_MASK_CAUSAL_ZIGZAG
+    assert lib.ra_plan_block(C.byref(d), 64, Z, 0, 3, C.byref(s)) == ra.RA_OK
+    assert lib.ra_plan_block(C.byref(d), 64, Z, 4, 0, C.byref(s)) == ra.RA_E_INVALID    # rank >= P
+    assert lib.ra_plan_block(C.byref(d), 64, Z, 0, -1, C.byref(s)) == ra.RA_E_INVALID
+    assert lib.ra_plan_block(C.byref(d), 32, Z, 0, 0, C.byref(s)) == ra.RA_E_INVALID    # kv_len != q_len
+    d_odd = _desc(q_len=63, P=4)
+    assert lib.ra_plan_block(C.byref(d_odd), 63, Z, 0, 0, C.byref(s)) == ra.RA_E_INVALID
+    assert lib.ra_plan_block(C.byref(d), 64, 4, 0, 0, C.byref(s)) == ra.RA_E_INVALID     # unknown mask
+
+
 @pytest.mark.parametrize("q_len,kv_len,q_off,k_off", [
     (200, 150, 0, 0), (200, 150, 149, 0), (200, 150, 0, 57), (1, 1, 0, 0), (1, 1, 0, 1),
     (129, 65, 3, 1), (64, 64, -10, 0), (300, 10, 1000, 0), (0, 64, 0, 0), (64, 0, 0, 0)])

@@ -18,8 +18,8 @@ from gpu_util import (assert_bf16_close, assert_f32_close, lap_with_steps, requi
 
 pytestmark = pytest.mark.gpu
 
-NONE, CONTIG, STRIPED = 0, 1, 2
-LAYOUT = {NONE: "contiguous", CONTIG: "contiguous", STRIPED: "striped"}
+NONE, CONTIG, STRIPED, ZIGZAG = 0, 1, 2, 3
+LAYOUT = {NONE: "contiguous", CONTIG: "contiguous", STRIPED: "striped", ZIGZAG: "zigzag"}
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -39,15 +39,15 @@ def _blocks(k, v, P, layout, dev="cuda"):
 # tiny exactness workload: N=256, P=4, one head, d=64, fp32
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("mask", [NONE, CONTIG])
+@pytest.mark.parametrize("mask", [NONE, CONTIG, ZIGZAG])
 @pytest.mark.parametrize("rank", [0, 1, 2, 3])
 def test_tiny_fp32_workload(mask, rank):
     w = synth.WORKLOADS["tiny_fp32_n256_p4"]
     q_all, k, v = synth.workload_tensors(w, rank)
     n = w.n_local
-    q_pos = oracle.tokens_of_rank(w.N, w.P, "contiguous", rank)
+    q_pos = oracle.tokens_of_rank(w.N, w.P, LAYOUT[mask], rank)
     q = q_all[:, :, q_pos].contiguous()
-    kb, vb = _blocks(k, v, w.P, "contiguous")
+    kb, vb = _blocks(k, v, w.P, LAYOUT[mask])
     say(f"  tiny fp32 rank={rank} mask={mask}")
     o, lse, stats = lap_with_steps(q.cuda(), kb, vb, rank, mask, w.P)
     torch.cuda.synchronize()
@@ -60,6 +60,8 @@ def test_tiny_fp32_workload(mask, rank):
     assert stats["live_pairs"] == pairs
     if mask == CONTIG:
         assert stats["blocks_skipped"] == w.P - 1 - rank
+    if mask == ZIGZAG:   # chunk 2P-1-r is later than every rank's first chunk: no block is empty
+        assert stats["blocks_skipped"] == 0
 
 
 # ---------------------------------------------------------------------------
@@ -77,6 +79,11 @@ CASES = [
     ("f32", 1, 2, 1, 128, 768, 4, 2, STRIPED),
     ("f32", 2, 4, 2, 64, 600, 3, 1, CONTIG),         # 200-token blocks
     ("f32", 1, 3, 3, 128, 500, 5, 4, NONE),          # 100-token blocks
+    ("bf16", 1, 4, 2, 128, 2048, 4, 1, ZIGZAG),      # 256-token chunks
+    ("bf16", 2, 2, 1, 128, 1800, 3, 2, ZIGZAG),      # 300-token chunks: ragged tiles
+    ("bf16", 1, 4, 4, 64, 1600, 4, 0, ZIGZAG),       # d = 64, 200-token chunks
+    ("f32", 1, 2, 1, 128, 1200, 3, 1, ZIGZAG),       # 200-token chunks
+    ("f32", 2, 2, 2, 64, 960, 4, 3, ZIGZAG),         # 120-token chunks
 ]
 
 
@@ -108,7 +115,8 @@ def test_random_small_lap(case):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
-@pytest.mark.parametrize("mask,rank", [(STRIPED, 1), (STRIPED, 6), (CONTIG, 5), (NONE, 2)])
+@pytest.mark.parametrize("mask,rank", [(STRIPED, 1), (STRIPED, 6), (CONTIG, 5), (NONE, 2), (ZIGZAG, 1),
+                                       (ZIGZAG, 6)])
 def test_lap_in_shuffled_block_order(dtype, mask, rank):
     """Blocks in a seeded random order: the first blocks may leave rows with no visible key
     (striped blocks after the rank's own), which the state must carry through unchanged."""
@@ -119,6 +127,11 @@ def test_lap_in_shuffled_block_order(dtype, mask, rank):
     kb, vb = _blocks(k, v, P, layout)
     order = [int(j) for j in np.random.default_rng(rank).permutation(P)]
     if mask == STRIPED:   # start with a block that sees strictly fewer keys than the rows
+        order.remove(P - 1)
+        order.insert(0, P - 1)
+    if mask == ZIGZAG and rank < P - 1:
+        # start with a block whose two chunks are both later than the rank's first chunk:
+        # that chunk's rows get no allowed pair in the first step of a fresh state
         order.remove(P - 1)
         order.insert(0, P - 1)
     say(f"  order {order}")
@@ -134,7 +147,7 @@ def test_lap_in_shuffled_block_order(dtype, mask, rank):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
-@pytest.mark.parametrize("mask", [CONTIG, STRIPED])
+@pytest.mark.parametrize("mask", [CONTIG, STRIPED, ZIGZAG])
 def test_mask_and_skip_decisions_bit_exact(dtype, mask):
     """The kernel's own counts of unmasked tiles, masked tiles and scored pairs equal the
     oracle's enumeration with the kernel's tile sizes, block by block."""
@@ -157,7 +170,13 @@ def test_mask_and_skip_decisions_bit_exact(dtype, mask):
         st.finalize()
         torch.cuda.synchronize()
         c = counters.cpu().tolist()
-        cls = oracle.tile_classes(q_pos, kp, plan["tile_q"], plan["tile_k"], True)
+        if mask == ZIGZAG:   # the kernel tiles each (query chunk, key chunk) pair on its own
+            cl = n // 2
+            cls = np.concatenate([oracle.tile_classes(q_pos[a * cl:(a + 1) * cl], kp[b * cl:(b + 1) * cl],
+                                                      plan["tile_q"], plan["tile_k"], True)
+                                  for a in range(2) for b in range(2)], axis=None)
+        else:
+            cls = oracle.tile_classes(q_pos, kp, plan["tile_q"], plan["tile_k"], True)
         want = [Hq * int((cls == oracle.FULL).sum()), Hq * int((cls == oracle.PARTIAL).sum()),
                 Hq * oracle.live_pair_count(q_pos, kp, True)]
         say(f"    block {j}: kernel {c} oracle {want}")
@@ -169,7 +188,7 @@ def test_mask_and_skip_decisions_bit_exact(dtype, mask):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
-@pytest.mark.parametrize("layout,mask", [("contiguous", CONTIG), ("striped", STRIPED)])
+@pytest.mark.parametrize("layout,mask", [("contiguous", CONTIG), ("striped", STRIPED), ("zigzag", ZIGZAG)])
 def test_single_visible_key_row_is_exact(dtype, layout, mask):
     """Global position 0 (rank 0, local row 0) may see only key 0: O = V[key 0] exactly."""
     N, P, d = 1024, 4, 128

@@ -14,7 +14,7 @@ from gpu_util import assert_bf16_close, oracle_rows, require_gpu, say, seeded_ro
 
 pytestmark = pytest.mark.gpu
 
-MASK_CODE = {"none": 0, "causal_contiguous": 1, "causal_striped": 2}
+MASK_CODE = {"none": 0, "causal_contiguous": 1, "causal_striped": 2, "causal_zigzag": 3}
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -45,6 +45,8 @@ FULL = [
     ("noncausal_n131072_p8_h32", 0, 1.0),      # the other reading: plain N(0,1) inputs
     ("causal_contig_n131072_p8_h32", 0, None),
     ("causal_contig_n131072_p8_h32", 7, None),
+    ("zigzag_n131072_p8_h32", 0, None),
+    ("zigzag_n131072_p8_h32", 7, None),
     ("striped_n262144_p16_h32", 5, None),
     ("gqa_striped_n1m_p64_h64kv8", 5, None),
 ]
