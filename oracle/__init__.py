@@ -26,6 +26,7 @@ from .attention import (  # noqa: F401
     brute_force_pair_count,
     dense_attention,
     live_pair_count,
+    merge_states,
     online_block_update,
     online_finalize,
     online_state_init,

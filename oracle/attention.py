@@ -30,6 +30,10 @@ state:
   chunks r and 2P-1-r ([P1] "Striping the sequence to flatten the triangle").
 * The causal rule is on global positions: query q sees key k iff k <= q ([P3]
   Causal Attention 让环不再完全对称, and 位置编码必须使用全局位置).
+* ``merge_states`` is the global online-softmax reduction of shard states for
+  decode ([P3] 训练与推理的适用方式不同: the query is sent to the KV shards, each
+  computes a local attention state, and the states are reduced), the same
+  rescale-and-add as a block update.
 * ``tile_classes`` enumerates pairs per (query tile, key tile) and names a tile
   EMPTY (no allowed pair), FULL (every pair allowed) or PARTIAL ([P3] Causal
   section's three-way block rule: strictly future -> skip, crossing the
@@ -230,6 +234,30 @@ def online_finalize(state: dict):
     out = np.where(seen[..., None], o / np.where(seen, l, 1.0)[..., None], 0.0)
     lse = np.where(seen, m + np.log(np.where(seen, l, 1.0)), -np.inf)
     return out, lse
+
+
+def merge_states(parts: Sequence[dict]) -> dict:
+    """Global online-softmax reduction of states over disjoint key sets (float64).
+
+    For decode the query goes to the KV shards, each shard computes a local
+    attention state, and one reduction combines them ([P3] 训练与推理的适用方式不同).
+    The combination is the same rescale-and-add as a block update ([P1] "Why
+    partial results are allowed to merge"): with m = max_s m_s,
+    l = sum_s exp(m_s - m) l_s and O~ = sum_s exp(m_s - m) O~_s.  Rows that no
+    part has seen stay at the empty state.
+    """
+    m = parts[0]["m"]
+    for st in parts[1:]:
+        m = np.maximum(m, st["m"])
+    live = np.isfinite(m)
+    m_safe = np.where(live, m, 0.0)
+    l = np.zeros_like(parts[0]["l"])
+    o = np.zeros_like(parts[0]["o"])
+    for st in parts:
+        w = np.where(np.isfinite(st["m"]), np.exp(st["m"] - m_safe), 0.0)
+        l = l + w * st["l"]
+        o = o + w[..., None] * st["o"]
+    return {"m": m, "l": l, "o": o}
 
 
 def blockwise_attention(q, blocks: Sequence[tuple], q_pos, causal: bool,

@@ -437,6 +437,62 @@ def test_live_pair_closed_forms_at_full_size(name, N, P, r, layout, per_head):
     assert total == per_head
 
 
+def _shard_state(q, k, v, q_pos, k_pos, keys, causal):
+    st = oracle.online_state_init(q.shape[0], q.shape[1], q.shape[2], v.shape[-1])
+    if keys.size:
+        st = oracle.online_block_update(st, q, k[:, :, keys], v[:, :, keys], q_pos, k_pos[keys], causal)
+    return st
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_merged_shard_states_equal_sdpa_over_all_keys(causal):
+    """Split-KV: disjoint random key shards, one state each, merged, equal exact attention
+    over every key (torch SDPA in float64; no oracle position or layout code involved)."""
+    rng = _rng(50)
+    N, d, Hq, Hkv, n = 96, 16, 4, 2, 7
+    q = rng.standard_normal((1, Hq, n, d))
+    k = rng.standard_normal((1, Hkv, N, d))
+    v = rng.standard_normal((1, Hkv, N, d))
+    q_pos = np.sort(rng.choice(N, size=n, replace=False)) if causal else np.arange(n)
+    k_pos = np.arange(N)
+    shard = rng.integers(0, 5, size=N)                       # 5 shards, random sizes
+    parts = [_shard_state(q, k, v, q_pos, k_pos, np.nonzero(shard == s)[0], causal) for s in range(5)]
+    o, lse = oracle.online_finalize(oracle.merge_states(parts))
+    kk = torch.from_numpy(np.repeat(k, Hq // Hkv, axis=1))
+    vv = torch.from_numpy(np.repeat(v, Hq // Hkv, axis=1))
+    mask = torch.from_numpy(k_pos[None, :] <= q_pos[:, None]) if causal else None
+    ref = F.scaled_dot_product_attention(torch.from_numpy(q), kk, vv, attn_mask=mask).numpy()
+    assert _rel(o, ref) <= 1e-12
+    # lse against a direct log-sum-exp over the allowed scores
+    s = np.einsum("bhnd,bhkd->bhnk", q, kk.numpy()) / math.sqrt(d)
+    if causal:
+        s = np.where(mask.numpy(), s, -np.inf)
+    ref_lse = np.log(np.exp(s - s.max(-1, keepdims=True)).sum(-1)) + s.max(-1)
+    assert np.max(np.abs(lse - ref_lse)) <= 1e-12
+
+
+def test_merge_order_empty_and_single_parts():
+    rng = _rng(51)
+    N, d, H, n = 64, 8, 2, 5
+    q = rng.standard_normal((1, H, n, d))
+    k = rng.standard_normal((1, H, N, d))
+    v = rng.standard_normal((1, H, N, d))
+    q_pos, k_pos = np.arange(n), np.arange(N)
+    parts = [_shard_state(q, k, v, q_pos, k_pos, np.arange(s, N, 3), False) for s in range(3)]
+    a = oracle.merge_states(parts)
+    b = oracle.merge_states(parts[::-1])
+    assert _rel(a["o"] / a["l"][..., None], b["o"] / b["l"][..., None]) <= 1e-14
+    # a single part and an added empty part leave the state exactly as it was
+    one = oracle.merge_states([parts[0]])
+    assert all(np.array_equal(one[x], parts[0][x]) for x in ("m", "l", "o"))
+    empty = oracle.online_state_init(1, H, n, d)
+    with_empty = oracle.merge_states([parts[1], empty])
+    assert all(np.array_equal(with_empty[x], parts[1][x]) for x in ("m", "l", "o"))
+    # rows no part has seen: O = 0 and lse = -inf after the merge
+    o, lse = oracle.online_finalize(oracle.merge_states([empty, empty]))
+    assert not o.any() and np.isneginf(lse).all()
+
+
 def test_zigzag_balances_the_causal_work():
     """[P1] "Striping the sequence to flatten the triangle": every rank gets one early and
     one late chunk, so the causal work is shared evenly.  Closed form: queries in chunk i
