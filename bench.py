@@ -141,6 +141,14 @@ def hbm_passes(ra, q, k, v, ws, w, desc, reps: int = 20):
                                "frac_of_8TB_s": round(nbytes / ms / 1e6 / PEAK_HBM_GBS, 3),
                                "TFLOP_s": round(flops / ms / 1e9, 1)}
     st.close()
+    # the reduction of shard states (split-KV decode): 8 parts of this state's size, here
+    # copies of the lap's state, into O and lse
+    parts = [ws] + [ws.clone() for _ in range(7)]
+    ms = timed(lambda: ra.merge_states(desc, parts, out=out, lse=lse))
+    nbytes = len(parts) * rows * (4 * d + 8) + rows * (4 * d + 4)
+    res["merge_8_parts"] = {"ms": round(ms, 4), "bytes": nbytes, "GB_s": round(nbytes / ms / 1e6, 1),
+                            "frac_of_8TB_s": round(nbytes / ms / 1e6 / PEAK_HBM_GBS, 3)}
+    del parts
     return res
 
 
@@ -153,6 +161,8 @@ def main() -> int:
     ap.add_argument("--rank", type=int, default=None, help="measured rank (default: the workload's first)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="oracle timing budget")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--hbm-passes", action="store_true",
+                    help="also time the HBM-bound passes (finalize, short KV blocks, state merge)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -245,7 +255,7 @@ def main() -> int:
         "avg_launch_ms": round(avg_kernel_ms, 4),
     }
 
-    hbm = hbm_passes(ra, qd, kb[0], vb[0], ws, w, desc)
+    hbm = hbm_passes(ra, qd, kb[0], vb[0], ws, w, desc) if args.hbm_passes else None
 
     cpu = None
     if not args.no_cpu_baseline:

@@ -24,6 +24,7 @@ from ._abi import (  # noqa: F401
     RA_MASK_CAUSAL_STRIPED,
     RA_MASK_CAUSAL_ZIGZAG,
     RA_MASK_NONE,
+    RA_MERGE_MAX_PARTS,
     RA_OK,
     RA_TILE_EMPTY,
     RA_TILE_FULL,
@@ -201,6 +202,17 @@ class RingState:
             self.close()
         except Exception:
             pass
+
+
+def merge_states(desc: ra_desc, parts, merged=None, out=None, lse=None) -> None:
+    """ra_merge_states: reduce the states held in the workspaces ``parts`` (torch uint8 device
+    tensors laid out for ``desc``) into the workspace ``merged`` and/or O and lse (fp32 device
+    tensors [B, Hq, n, d] and [B, Hq, n]), on desc.stream."""
+    arr = (C.c_void_p * len(parts))(*[w.data_ptr() for w in parts])
+    check(lib().ra_merge_states(C.byref(desc), len(parts), arr,
+                                merged.data_ptr() if merged is not None else None,
+                                out.data_ptr() if out is not None else None,
+                                lse.data_ptr() if lse is not None else None))
 
 
 def block_offsets(mask_kind: int, rank: int, block: int, q_len: int, kv_len: int) -> tuple[int, int]:

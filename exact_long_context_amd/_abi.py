@@ -23,6 +23,7 @@ RA_MASK_NONE = 0
 RA_MASK_CAUSAL_CONTIGUOUS = 1
 RA_MASK_CAUSAL_STRIPED = 2
 RA_MASK_CAUSAL_ZIGZAG = 3
+RA_MERGE_MAX_PARTS = 64
 
 RA_DTYPE_BF16 = 0
 RA_DTYPE_F32 = 1
@@ -90,6 +91,8 @@ SIGNATURES = {
     "ra_block_step": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_int32, C.c_int32,
                                 C.c_int64, C.c_int64]),
     "ra_finalize": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p]),
+    "ra_merge_states": (C.c_int, [C.POINTER(ra_desc), C.c_int32, C.POINTER(C.c_void_p), C.c_void_p,
+                                  C.c_void_p, C.c_void_p]),
     "ra_state_destroy": (C.c_int, [C.c_void_p]),
     "ra_get_stats": (C.c_int, [C.c_void_p, C.POINTER(ra_stats)]),
     "ra_state_set_debug_counters": (C.c_int, [C.c_void_p, C.c_void_p]),

@@ -29,6 +29,7 @@ SOURCES = [
     "ra_step_bf16.hip",
     "ra_step_f32.hip",
     "ra_finalize.hip",
+    "ra_merge.hip",
 ]
 
 ARCH = "gfx950"

@@ -352,6 +352,41 @@ int ra_finalize(ra_state* st, float* o, float* lse) {
   return RA_OK;
 }
 
+int ra_merge_states(const ra_desc* desc, int32_t n_parts, void* const* parts, void* merged,
+                    float* o, float* lse) {
+  int rc = check_desc(desc);
+  if (rc) return rc;
+  if (n_parts < 1 || n_parts > RA_MERGE_MAX_PARTS)
+    return fail(RA_E_INVALID, "n_parts %d is outside [1, %d]", n_parts, RA_MERGE_MAX_PARTS);
+  if (!parts) return fail(RA_E_INVALID, "parts is NULL");
+  if (!merged && !o) return fail(RA_E_INVALID, "neither a merged state nor O requested");
+  if (lse && !o) return fail(RA_E_INVALID, "lse is written together with O only");
+  const int64_t rows = (int64_t)desc->batch * desc->q_heads * desc->q_len;
+  for (int s = 0; s < n_parts; ++s) {
+    if (rows > 0 && !parts[s]) return fail(RA_E_INVALID, "parts[%d] is NULL", s);
+    if ((reinterpret_cast<uintptr_t>(parts[s]) & 255) != 0)
+      return fail(RA_E_INVALID, "parts[%d] must be 256-byte aligned", s);
+  }
+  if (merged && (reinterpret_cast<uintptr_t>(merged) & 255) != 0)
+    return fail(RA_E_INVALID, "merged must be 256-byte aligned");
+  if (o && !aligned16(o)) return fail(RA_E_INVALID, "O must be 16-byte aligned");
+  const Layout L = layout_of(desc);
+  ra::MergeParams p;
+  std::memset(&p, 0, sizeof p);
+  for (int s = 0; s < n_parts; ++s) p.parts[s] = static_cast<const char*>(parts[s]);
+  p.n_parts = n_parts;
+  p.m_off = L.m_off;
+  p.l_off = L.l_off;
+  p.merged = static_cast<char*>(merged);
+  p.o = o;
+  p.lse = lse;
+  p.rows = rows;
+  p.d = desc->head_dim;
+  hipError_t e = ra::launch_merge(p, static_cast<hipStream_t>(desc->stream));
+  if (e != hipSuccess) return hip_fail(e, "merge kernel launch");
+  return RA_OK;
+}
+
 int ra_state_destroy(ra_state* st) {
   delete st;
   return RA_OK;

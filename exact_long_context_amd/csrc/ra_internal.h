@@ -40,6 +40,21 @@ struct FinalizeParams {
   int32_t fresh;       // 1: no step ever ran; write the empty result without reading
 };
 
+// The reduction of shard states: every part is a workspace laid out like the state (O~ at
+// byte 0, m at m_off, l at l_off); the merged state goes to `merged` (same layout) and/or
+// O and lse to o, lse.  Null outputs are skipped.
+constexpr int kMergeMaxParts = 64;
+struct MergeParams {
+  const char* parts[kMergeMaxParts];
+  int32_t n_parts;
+  size_t m_off, l_off;
+  char* merged;
+  float* o;
+  float* lse;
+  int64_t rows;        // B * Hq * n
+  int32_t d;
+};
+
 // Tile sizes of each kernel (the planner reports and classifies with these).
 constexpr int kBf16TileQ = 128;
 constexpr int kBf16TileK = 64;
@@ -49,5 +64,6 @@ constexpr int kF32TileK = 32;
 hipError_t launch_step_bf16(const StepParams& p, int head_dim, hipStream_t stream);
 hipError_t launch_step_f32(const StepParams& p, int head_dim, hipStream_t stream);
 hipError_t launch_finalize(const FinalizeParams& p, hipStream_t stream);
+hipError_t launch_merge(const MergeParams& p, hipStream_t stream);
 
 }  // namespace ra

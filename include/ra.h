@@ -175,6 +175,27 @@ int ra_get_stats(const ra_state* st, ra_stats* out);
  * pairs it actually scored.  NULL switches counting off. */
 int ra_state_set_debug_counters(ra_state* st, uint64_t* counters);
 
+/* ---- reduction of shard states (split-KV decode) ---------------------------------- */
+
+#define RA_MERGE_MAX_PARTS 64
+
+/* Merge n_parts states of the same query rows, each over a disjoint set of keys, into one
+ * ("Ring Attention：把超长序列沿设备环流动", section 训练与推理的适用方式不同: for decode the query is
+ * sent to the KV shards, each computes a local attention state, and a global online-softmax
+ * reduction combines them; the combination is the rescale-and-add of "GPU ring attention",
+ * section "Why partial results are allowed to merge"):
+ *     m = max_s m_s,   l = sum_s e^(m_s - m) l_s,   O~ = sum_s e^(m_s - m) O~_s.
+ * parts: host array of n_parts (1 <= n_parts <= RA_MERGE_MAX_PARTS) device workspaces, each
+ * laid out as ra_workspace_layout(desc) gives and holding a valid state of these rows: one
+ * written by at least one launch of ra_block_step (ra_get_stats: blocks_run > 0); a state
+ * whose blocks were all skipped holds nothing yet and must be left out.  Outputs (device,
+ * each may be NULL but not both merged and o): merged, a workspace (256-byte aligned, it may
+ * be one of the parts) that receives the merged state, and o / lse, which receive
+ * O = O~ / l and lse exactly as ra_finalize would write them for the merged state (lse only
+ * together with o).  Enqueued on desc.stream. */
+int ra_merge_states(const ra_desc* desc, int32_t n_parts, void* const* parts, void* merged,
+                    float* o, float* lse);
+
 /* ---- host-only planner (no device work; safe without a GPU) ------------------------ */
 
 /* What ra_block_step would do for this block, as counts for the whole launch. */

@@ -286,6 +286,28 @@ def test_fully_masked_blocks_launch_nothing():
     lib.ra_state_destroy(h)
 
 
+def test_merge_argument_validation():
+    # every check happens on the host before anything is enqueued
+    lib = ra.lib()
+    d = _desc(q_len=64)
+    ok = 0x100000
+    parts = (C.c_void_p * 2)(ok, ok + 0x100000)
+    E = ra.RA_E_INVALID
+    assert lib.ra_merge_states(C.byref(d), 0, parts, ok, None, None) == E             # no parts
+    big = (C.c_void_p * 65)(*([ok] * 65))
+    assert lib.ra_merge_states(C.byref(d), 65, big, ok, None, None) == E              # too many
+    assert lib.ra_merge_states(C.byref(d), 2, None, ok, None, None) == E              # NULL array
+    assert lib.ra_merge_states(C.byref(d), 2, parts, None, None, None) == E           # no output
+    assert lib.ra_merge_states(C.byref(d), 2, parts, ok, None, ok) == E               # lse without O
+    bad = (C.c_void_p * 2)(ok, ok + 64)
+    assert lib.ra_merge_states(C.byref(d), 2, bad, ok, None, None) == E               # misaligned part
+    nul = (C.c_void_p * 2)(ok, None)
+    assert lib.ra_merge_states(C.byref(d), 2, nul, ok, None, None) == E               # NULL part
+    assert lib.ra_merge_states(C.byref(d), 2, parts, ok + 16, None, None) == E        # misaligned merged
+    assert lib.ra_merge_states(C.byref(d), 2, parts, None, ok + 4, None) == E         # misaligned O
+    assert ra.RA_MERGE_MAX_PARTS == 64
+
+
 def test_lap_argument_validation():
     lib = ra.lib()
     d = _desc(q_len=64, P=4)
