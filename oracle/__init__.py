@@ -22,6 +22,8 @@ from .attention import (  # noqa: F401
     FULL,
     PARTIAL,
     allowed_mask,
+    backward_block,
+    backward_row_terms,
     blockwise_attention,
     brute_force_pair_count,
     dense_attention,

@@ -34,6 +34,11 @@ state:
   decode ([P3] 训练与推理的适用方式不同: the query is sent to the KV shards, each
   computes a local attention state, and the states are reduced), the same
   rescale-and-add as a block update.
+* ``backward_row_terms`` / ``backward_block`` are one ring step of the backward
+  pass ([P3] Backward 需要让梯度也沿环传播: dQ stays with the query owner, dK and dV
+  accumulate on the travelling block, probabilities are recomputed from the saved
+  per-row logsumexp); the gradient formulas are the standard ones, not printed on
+  the pages.
 * ``tile_classes`` enumerates pairs per (query tile, key tile) and names a tile
   EMPTY (no allowed pair), FULL (every pair allowed) or PARTIAL ([P3] Causal
   section's three-way block rule: strictly future -> skip, crossing the
@@ -275,6 +280,56 @@ def blockwise_attention(q, blocks: Sequence[tuple], q_pos, causal: bool,
         k_j, v_j, kp = blocks[j]
         st = online_block_update(st, q, k_j, v_j, q_pos, kp, causal, scale)
     return online_finalize(st)
+
+
+# ----------------------------------------------------------------------------
+# Backward: gradients of one rank's lap, block by block
+# ----------------------------------------------------------------------------
+
+def backward_row_terms(d_out, out):
+    """D_i = sum_c dO[i, c] * O[i, c]: the per-row term of the softmax gradient."""
+    return np.einsum("bhnd,bhnd->bhn", np.asarray(d_out, np.float64), np.asarray(out, np.float64))
+
+
+def backward_block(q, k_j, v_j, d_out, lse, D, q_pos, k_pos_j, causal: bool,
+                   scale: float | None = None):
+    """One ring step of the backward pass (float64): this query shard's contribution to
+    dQ and to the travelling block's dK_j, dV_j.
+
+    [P3] Backward 需要让梯度也沿环传播: the query owner accumulates dQ over every KV
+    block; dK, dV of a travelling block accumulate over the query owners it passes; the
+    probabilities are recomputed per block from the saved per-row logsumexp instead of
+    storing the attention matrix.  The gradient of softmax attention (not printed on the
+    pages; the standard form) with P = exp(scale * q.k - lse) on allowed pairs:
+        dV_j = P^T dO,   dP = dO V_j^T,   dS = P * (dP - D),
+        dQ   = scale * dS K_j,   dK_j = scale * dS^T Q.
+    Query head h reads (and writes gradients to) KV head h // (Hq / Hkv).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k_j = np.asarray(k_j, dtype=np.float64)
+    v_j = np.asarray(v_j, dtype=np.float64)
+    d_out = np.asarray(d_out, dtype=np.float64)
+    B, Hq, n, d = q.shape
+    Hkv = k_j.shape[1]
+    G = _group(Hq, Hkv)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    ok = allowed_mask(q_pos, k_pos_j, causal)
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k_j)
+    dv = np.zeros((B, Hkv, k_j.shape[2], v_j.shape[-1]))
+    for b in range(B):
+        for h in range(Hq):
+            g = h // G
+            s = scale * (q[b, h] @ k_j[b, g].T)
+            fin = np.isfinite(lse[b, h])[:, None]
+            p = np.where(ok & fin, np.exp(s - np.where(fin, lse[b, h][:, None], 0.0)), 0.0)
+            dv[b, g] += p.T @ d_out[b, h]
+            dp = d_out[b, h] @ v_j[b, g].T
+            ds = p * (dp - D[b, h][:, None])
+            dq[b, h] += scale * (ds @ k_j[b, g])
+            dk[b, g] += scale * (ds.T @ q[b, h])
+    return dq, dk, dv
 
 
 # ----------------------------------------------------------------------------

@@ -493,6 +493,80 @@ def test_merge_order_empty_and_single_parts():
     assert not o.any() and np.isneginf(lse).all()
 
 
+@pytest.mark.parametrize("layout", ["contiguous", "striped", "zigzag"])
+@pytest.mark.parametrize("Hq,Hkv", [(2, 2), (4, 2)])
+def test_ring_backward_sums_to_autograd(layout, Hq, Hkv):
+    """Every rank's dQ (summed over its lap's blocks) and every block's dK, dV (summed over
+    the ranks it visits) equal torch autograd of causal attention on the whole sequence, in
+    float64; the forward lse and O come from torch too, so no oracle forward is involved."""
+    rng = _rng(70 + Hq)
+    N, P, d = 48, 4, 8
+    G = Hq // Hkv
+    q = torch.from_numpy(rng.standard_normal((1, Hq, N, d))).requires_grad_()
+    k = torch.from_numpy(rng.standard_normal((1, Hkv, N, d))).requires_grad_()
+    v = torch.from_numpy(rng.standard_normal((1, Hkv, N, d))).requires_grad_()
+    d_out = torch.from_numpy(rng.standard_normal((1, Hq, N, d)))
+    kk, vv = k.repeat_interleave(G, dim=1), v.repeat_interleave(G, dim=1)
+    mask = torch.tril(torch.ones(N, N, dtype=torch.bool))
+    s = (q @ kk.transpose(-1, -2)) / math.sqrt(d)
+    s = s.masked_fill(~mask, -math.inf)
+    out = torch.softmax(s, -1) @ vv
+    lse = torch.logsumexp(s, -1).detach().numpy()
+    out.backward(d_out)
+    q_np, k_np, v_np, do_np = q.detach().numpy(), k.detach().numpy(), v.detach().numpy(), d_out.numpy()
+    o_np = out.detach().numpy()
+    dq = np.zeros_like(q_np)
+    dk = np.zeros_like(k_np)
+    dv = np.zeros_like(v_np)
+    for r in range(P):
+        qp = oracle.tokens_of_rank(N, P, layout, r)
+        D = oracle.backward_row_terms(do_np[:, :, qp], o_np[:, :, qp])
+        for j in oracle.ring_visit_order(P, r):
+            kp = oracle.tokens_of_rank(N, P, layout, j)
+            gq, gk, gv = oracle.backward_block(q_np[:, :, qp], k_np[:, :, kp], v_np[:, :, kp],
+                                               do_np[:, :, qp], lse[:, :, qp], D, qp, kp, True)
+            dq[:, :, qp] += gq
+            dk[:, :, kp] += gk
+            dv[:, :, kp] += gv
+    assert _rel(dq, q.grad.numpy()) <= 1e-12
+    assert _rel(dk, k.grad.numpy()) <= 1e-12
+    assert _rel(dv, v.grad.numpy()) <= 1e-12
+
+
+def test_backward_terms_against_scalar_loops():
+    """D and one block's gradients written out as scalar Python loops over the pairs."""
+    rng = _rng(71)
+    n, nk, d = 3, 4, 2
+    q = rng.standard_normal((1, 1, n, d))
+    k = rng.standard_normal((1, 1, nk, d))
+    v = rng.standard_normal((1, 1, nk, d))
+    do = rng.standard_normal((1, 1, n, d))
+    o = rng.standard_normal((1, 1, n, d))
+    q_pos, k_pos = np.array([1, 2, 3]), np.array([0, 1, 2, 3])
+    sc = 0.7
+    lse = rng.standard_normal((1, 1, n)) + 2.0
+    D = oracle.backward_row_terms(do, o)
+    for i in range(n):
+        assert abs(D[0, 0, i] - sum(do[0, 0, i, c] * o[0, 0, i, c] for c in range(d))) <= 1e-14
+    gq, gk, gv = oracle.backward_block(q, k, v, do, lse, D, q_pos, k_pos, True, scale=sc)
+    eq, ek, ev = np.zeros((n, d)), np.zeros((nk, d)), np.zeros((nk, d))
+    for i in range(n):
+        for t in range(nk):
+            if k_pos[t] > q_pos[i]:
+                continue
+            s_it = sc * sum(q[0, 0, i, c] * k[0, 0, t, c] for c in range(d))
+            p_it = math.exp(s_it - lse[0, 0, i])
+            dp_it = sum(do[0, 0, i, c] * v[0, 0, t, c] for c in range(d))
+            ds_it = p_it * (dp_it - D[0, 0, i])
+            for c in range(d):
+                ev[t, c] += p_it * do[0, 0, i, c]
+                eq[i, c] += sc * ds_it * k[0, 0, t, c]
+                ek[t, c] += sc * ds_it * q[0, 0, i, c]
+    assert np.max(np.abs(gq[0, 0] - eq)) <= 1e-13
+    assert np.max(np.abs(gk[0, 0] - ek)) <= 1e-13
+    assert np.max(np.abs(gv[0, 0] - ev)) <= 1e-13
+
+
 def test_zigzag_balances_the_causal_work():
     """[P1] "Striping the sequence to flatten the triangle": every rank gets one early and
     one late chunk, so the causal work is shared evenly.  Closed form: queries in chunk i
