@@ -215,6 +215,62 @@ def merge_states(desc: ra_desc, parts, merged=None, out=None, lse=None) -> None:
                                 lse.data_ptr() if lse is not None else None))
 
 
+class RingBackward:
+    """The backward of one rank's lap (ra_bwd_init / ra_bwd_block_step / ra_bwd_finalize).
+
+    ``q`` and ``d_out`` are Q_r and dO_r (same dtype and strides), ``out`` and ``lse`` the
+    forward's O_r and lse_r (fp32, as ``RingState.finalize`` returns them); ``kv_like`` any
+    tensor with the KV blocks' shape and strides.
+    """
+
+    def __init__(self, q, d_out, out, lse, kv_like, ring_size: int = 1, softmax_scale: float = 0.0,
+                 workspace=None, stream=None):
+        import torch
+        if d_out.dtype != q.dtype or d_out.stride() != q.stride() or d_out.shape != q.shape:
+            raise ValueError("dO_r must have Q_r's shape, dtype and strides")
+        self.q, self.d_out, self.out, self.lse = q, d_out, out.contiguous(), lse.contiguous()
+        self.desc = desc_for(q, kv_like, ring_size, softmax_scale, stream)
+        nbytes = lib().ra_bwd_workspace_bytes(C.byref(self.desc))
+        if workspace is None:
+            workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=q.device)
+        self.workspace = workspace
+        h = C.c_void_p()
+        check(lib().ra_bwd_init(C.byref(self.desc), q.data_ptr(), d_out.data_ptr(), self.out.data_ptr(),
+                                self.lse.data_ptr(), workspace.data_ptr(), C.byref(h)))
+        self._h = h
+
+    def step(self, k, v, dk, dv, mask_kind: int, q_offset: int = 0, k_offset: int = 0) -> None:
+        if k.stride() != v.stride() or tuple(k.stride()[:3]) != tuple(self.desc.kv_strides):
+            raise ValueError("K and V must have the strides the state was created for")
+        if not (dk.is_contiguous() and dv.is_contiguous()) or dk.shape != k.shape or dv.shape != v.shape:
+            raise ValueError("dK and dV must be contiguous fp32 tensors of the block's shape")
+        check(lib().ra_bwd_block_step(self._h, k.data_ptr(), v.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                                      k.shape[2], mask_kind, q_offset, k_offset))
+
+    def finalize(self, dq=None):
+        import torch
+        if dq is None:
+            dq = torch.empty(self.q.shape, dtype=torch.float32, device=self.q.device)
+        check(lib().ra_bwd_finalize(self._h, dq.data_ptr()))
+        return dq
+
+    def stats(self) -> dict:
+        s = ra_stats()
+        check(lib().ra_bwd_get_stats(self._h, C.byref(s)))
+        return s.as_dict()
+
+    def close(self) -> None:
+        if self._h is not None:
+            lib().ra_bwd_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
 def block_offsets(mask_kind: int, rank: int, block: int, q_len: int, kv_len: int) -> tuple[int, int]:
     """(q_offset, k_offset) of a block under a mask's layout (include/ra.h conventions)."""
     if mask_kind == RA_MASK_CAUSAL_CONTIGUOUS:

@@ -30,6 +30,19 @@ struct ra_state {
   unsigned long long* dbg;
 };
 
+// The backward of one rank's lap: the resident Q_r and dO_r, the forward's lse_r, and the
+// workspace holding the dQ accumulator and D = rowsum(dO * O).
+struct ra_bwd {
+  ra_desc desc;
+  const void* q;
+  const void* d_out;
+  const float* lse;
+  float* dq;
+  float* D;
+  int finalized;
+  ra_stats stats;
+};
+
 namespace {
 
 thread_local char g_err[256] = "";
@@ -384,6 +397,151 @@ int ra_merge_states(const ra_desc* desc, int32_t n_parts, void* const* parts, vo
   p.d = desc->head_dim;
   hipError_t e = ra::launch_merge(p, static_cast<hipStream_t>(desc->stream));
   if (e != hipSuccess) return hip_fail(e, "merge kernel launch");
+  return RA_OK;
+}
+
+size_t ra_bwd_workspace_bytes(const ra_desc* desc) {
+  if (check_desc(desc)) return 0;
+  const size_t rows = (size_t)desc->batch * desc->q_heads * desc->q_len;
+  return rows ? align256(rows * desc->head_dim * sizeof(float)) + align256(rows * sizeof(float)) : 0;
+}
+
+int ra_bwd_init(const ra_desc* desc, const void* q, const void* d_out, const float* out,
+                const float* lse, void* workspace, ra_bwd** handle) {
+  if (!handle) return fail(RA_E_INVALID, "out is NULL");
+  *handle = nullptr;
+  int rc = check_desc(desc);
+  if (rc) return rc;
+  const int64_t rows = (int64_t)desc->batch * desc->q_heads * desc->q_len;
+  if (rows > 0) {
+    if (!q || !d_out || !out || !lse || !workspace)
+      return fail(RA_E_INVALID, "Q_r, dO_r, O_r, lse_r and the workspace are required");
+    if (!aligned16(q) || !aligned16(d_out) || !aligned16(out))
+      return fail(RA_E_INVALID, "Q_r, dO_r and O_r must be 16-byte aligned");
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255) != 0)
+      return fail(RA_E_INVALID, "workspace must be 256-byte aligned");
+  }
+  ra_bwd* st = new (std::nothrow) ra_bwd;
+  if (!st) return fail(RA_E_INVALID, "out of host memory");
+  std::memset(st, 0, sizeof *st);
+  st->desc = *desc;
+  if (st->desc.softmax_scale == 0.f) st->desc.softmax_scale = 1.0f / std::sqrt((float)desc->head_dim);
+  st->q = q;
+  st->d_out = d_out;
+  st->lse = lse;
+  char* base = static_cast<char*>(workspace);
+  st->dq = reinterpret_cast<float*>(base);
+  st->D = reinterpret_cast<float*>(base + align256((size_t)rows * desc->head_dim * sizeof(float)));
+  st->stats.tile_q = 64;
+  st->stats.tile_k = 64;
+  if (rows > 0) {
+    ra::BwdPrepParams pp;
+    pp.d_out = d_out;
+    pp.out = out;
+    pp.D = st->D;
+    pp.dq = st->dq;
+    pp.q_sb = desc->q_strides[0];
+    pp.q_sh = desc->q_strides[1];
+    pp.q_st = desc->q_strides[2];
+    pp.q_heads = desc->q_heads;
+    pp.n_q = desc->q_len;
+    pp.rows = rows;
+    hipError_t e = ra::launch_bwd_prep(pp, desc->head_dim, desc->dtype == RA_DTYPE_BF16,
+                                       static_cast<hipStream_t>(desc->stream));
+    if (e != hipSuccess) {
+      delete st;
+      return hip_fail(e, "backward prep launch");
+    }
+  }
+  *handle = st;
+  return RA_OK;
+}
+
+int ra_bwd_block_step(ra_bwd* st, const void* k, const void* v, float* dk, float* dv,
+                      int32_t kv_len, int32_t mask_kind, int64_t q_offset, int64_t k_offset) {
+  if (!st) return fail(RA_E_INVALID, "state is NULL");
+  if (st->finalized) return fail(RA_E_STATE, "step after finalize");
+  const ra_desc* d = &st->desc;
+  ra_stats s;
+  Sub subs[4];
+  int n_subs = 0;
+  int rc = plan(d, kv_len, mask_kind, q_offset, k_offset, &s, subs, &n_subs);
+  if (rc) return rc;
+  if (kv_len > 0) {
+    if (!k || !v || !dk || !dv) return fail(RA_E_INVALID, "K_j, V_j, dK_j or dV_j is NULL");
+    if (!aligned16(k) || !aligned16(v) || !aligned16(dk) || !aligned16(dv))
+      return fail(RA_E_INVALID, "K_j, V_j, dK_j and dV_j must be 16-byte aligned");
+    if (kv_len > 1 && d->kv_strides[2] < d->head_dim)
+      return fail(RA_E_INVALID, "kv token stride smaller than head_dim");
+  }
+  s.tile_q = st->stats.tile_q;
+  s.tile_k = st->stats.tile_k;
+  s.tiles_full = s.tiles_partial = s.tiles_empty = 0;   // the backward kernels tile differently
+  if (s.blocks_run == 0) {
+    add_stats(&st->stats, &s);
+    return RA_OK;
+  }
+  const size_t elem = d->dtype == RA_DTYPE_BF16 ? 2 : 4;
+  for (int u = 0; u < n_subs; ++u) {
+    const Sub& b = subs[u];
+    if (b.pairs == 0) continue;
+    ra::BwdParams p;
+    p.q = static_cast<const char*>(st->q) + (int64_t)b.row0 * d->q_strides[2] * elem;
+    p.d_out = static_cast<const char*>(st->d_out) + (int64_t)b.row0 * d->q_strides[2] * elem;
+    p.k = static_cast<const char*>(k) + (int64_t)b.key0 * d->kv_strides[2] * elem;
+    p.v = static_cast<const char*>(v) + (int64_t)b.key0 * d->kv_strides[2] * elem;
+    p.lse = st->lse + b.row0;
+    p.D = st->D + b.row0;
+    p.dq = st->dq + (int64_t)b.row0 * d->head_dim;
+    p.dk = dk + (int64_t)b.key0 * d->head_dim;
+    p.dv = dv + (int64_t)b.key0 * d->head_dim;
+    p.q_sb = d->q_strides[0];
+    p.q_sh = d->q_strides[1];
+    p.q_st = d->q_strides[2];
+    p.k_sb = d->kv_strides[0];
+    p.k_sh = d->kv_strides[1];
+    p.k_st = d->kv_strides[2];
+    p.batch = d->batch;
+    p.q_heads = d->q_heads;
+    p.kv_heads = d->kv_heads;
+    p.group = d->q_heads / d->kv_heads;
+    p.n_q = b.rows;
+    p.n_k = b.keys;
+    p.state_rows = d->q_len;
+    p.dkv_rows = kv_len;
+    p.diag = b.diag;
+    p.scale = d->softmax_scale;
+    hipError_t e = ra::launch_bwd_step_valu(p, d->head_dim, d->dtype == RA_DTYPE_BF16,
+                                            static_cast<hipStream_t>(d->stream));
+    if (e != hipSuccess) return hip_fail(e, "backward step launch");
+  }
+  add_stats(&st->stats, &s);
+  return RA_OK;
+}
+
+int ra_bwd_finalize(ra_bwd* st, float* dq) {
+  if (!st) return fail(RA_E_INVALID, "state is NULL");
+  if (st->finalized) return fail(RA_E_STATE, "state already finalized");
+  const ra_desc* d = &st->desc;
+  const size_t bytes = (size_t)d->batch * d->q_heads * d->q_len * d->head_dim * sizeof(float);
+  if (bytes > 0) {
+    if (!dq) return fail(RA_E_INVALID, "dQ_r is NULL");
+    hipError_t e = hipMemcpyAsync(dq, st->dq, bytes, hipMemcpyDeviceToDevice,
+                                  static_cast<hipStream_t>(d->stream));
+    if (e != hipSuccess) return hip_fail(e, "dQ copy");
+  }
+  st->finalized = 1;
+  return RA_OK;
+}
+
+int ra_bwd_get_stats(const ra_bwd* st, ra_stats* out) {
+  if (!st || !out) return fail(RA_E_INVALID, "state or out is NULL");
+  *out = st->stats;
+  return RA_OK;
+}
+
+int ra_bwd_destroy(ra_bwd* st) {
+  delete st;
   return RA_OK;
 }
 

@@ -55,6 +55,37 @@ struct MergeParams {
   int32_t d;
 };
 
+// Backward: D = rowsum(dO * O) for every row of the state, and the dQ accumulator cleared.
+struct BwdPrepParams {
+  const void* d_out;   // [B, Hq, n, d] in the input dtype, Q's strides
+  const float* out;    // O from the forward finalize, fp32 [B, Hq, n, d] contiguous
+  float* D;            // [B, Hq, n]
+  float* dq;           // [B, Hq, n, d]
+  int64_t q_sb, q_sh, q_st;
+  int32_t q_heads, n_q;
+  int64_t rows;        // B * Hq * n
+};
+
+// One backward launch: rows [0, n_q) of q, d_out, lse, D, dq (a sub-range of the state, of
+// state_rows rows per head) against keys [0, n_k) of k, v, dk, dv (of dkv_rows keys per head).
+struct BwdParams {
+  const void* q;
+  const void* d_out;
+  const void* k;
+  const void* v;
+  const float* lse;    // natural-log logsumexp of the forward, [.., state_rows]
+  const float* D;
+  float* dq;           // fp32 [.., state_rows, d]
+  float* dk;           // fp32 [B, Hkv, dkv_rows, d]
+  float* dv;
+  int64_t q_sb, q_sh, q_st;
+  int64_t k_sb, k_sh, k_st;
+  int32_t batch, q_heads, kv_heads, group;
+  int32_t n_q, n_k, state_rows, dkv_rows;
+  int32_t diag;
+  float scale;
+};
+
 // Tile sizes of each kernel (the planner reports and classifies with these).
 constexpr int kBf16TileQ = 128;
 constexpr int kBf16TileK = 64;
@@ -65,5 +96,7 @@ hipError_t launch_step_bf16(const StepParams& p, int head_dim, hipStream_t strea
 hipError_t launch_step_f32(const StepParams& p, int head_dim, hipStream_t stream);
 hipError_t launch_finalize(const FinalizeParams& p, hipStream_t stream);
 hipError_t launch_merge(const MergeParams& p, hipStream_t stream);
+hipError_t launch_bwd_prep(const BwdPrepParams& p, int head_dim, bool bf16, hipStream_t stream);
+hipError_t launch_bwd_step_valu(const BwdParams& p, int head_dim, bool bf16, hipStream_t stream);
 
 }  // namespace ra

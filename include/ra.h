@@ -196,6 +196,47 @@ int ra_state_set_debug_counters(ra_state* st, uint64_t* counters);
 int ra_merge_states(const ra_desc* desc, int32_t n_parts, void* const* parts, void* merged,
                     float* o, float* lse);
 
+/* ---- backward of the lap ------------------------------------------------------------ */
+
+/* The backward pass runs the same lap with gradients travelling too ("Ring Attention：把超长序
+ * 列沿设备环流动", section Backward 需要让梯度也沿环传播): the query owner accumulates dQ_r over every
+ * KV block; the travelling block carries dK_j, dV_j, to which every query owner it passes
+ * adds its contribution; the probabilities are recomputed per block from the forward's saved
+ * per-row logsumexp.  With P = exp(scale * <q, k> - lse) on allowed pairs (the standard
+ * gradient of softmax attention, not printed on the page):
+ *     D = rowsum(dO * O),  dV_j += P^T dO,  dS = P * (dO V_j^T - D),
+ *     dQ += scale * dS K_j,  dK_j += scale * dS^T Q.
+ * Query head h adds to KV head h / (q_heads / kv_heads), as in the forward. */
+typedef struct ra_bwd ra_bwd;   /* opaque host object */
+
+/* Bytes of the backward workspace: the fp32 dQ accumulator [B, Hq, n, d] and D [B, Hq, n]. */
+size_t ra_bwd_workspace_bytes(const ra_desc* desc);
+
+/* Bind the backward of one rank's lap.  q: Q_r as for ra_state_init; d_out: dO_r, the
+ * gradient of the forward output, in desc.dtype with Q_r's strides; out and lse: O_r and
+ * lse_r as ra_finalize wrote them (fp32 contiguous, device); workspace: device,
+ * 256-byte aligned, ra_bwd_workspace_bytes(desc) bytes.  Enqueues D = rowsum(dO * O) and
+ * clears the dQ accumulator.  All of them must stay valid until ra_bwd_finalize. */
+int ra_bwd_init(const ra_desc* desc, const void* q, const void* d_out, const float* out,
+                const float* lse, void* workspace, ra_bwd** out_handle);
+
+/* One backward ring step against KV block (k, v), with the block's travelling gradients dk,
+ * dv (fp32 device [B, Hkv, kv_len, d] contiguous, accumulated into: they start at zero where
+ * the block begins its lap).  kv_len, mask_kind and the offsets are those of the forward
+ * ra_block_step for the same block; a block with no allowed pair launches nothing. */
+int ra_bwd_block_step(ra_bwd* st, const void* k, const void* v, float* dk, float* dv,
+                      int32_t kv_len, int32_t mask_kind, int64_t q_offset, int64_t k_offset);
+
+/* dQ_r = the accumulated gradient, fp32 [B, Hq, n, d] contiguous (device).  Afterwards the
+ * state takes no more steps (RA_E_STATE). */
+int ra_bwd_finalize(ra_bwd* st, float* dq);
+
+/* Host-side counts over this backward's steps (live pairs, blocks run and skipped). */
+int ra_bwd_get_stats(const ra_bwd* st, ra_stats* out);
+
+/* Release the host object. */
+int ra_bwd_destroy(ra_bwd* st);
+
 /* ---- host-only planner (no device work; safe without a GPU) ------------------------ */
 
 /* What ra_block_step would do for this block, as counts for the whole launch. */
