@@ -152,6 +152,42 @@ def hbm_passes(ra, q, k, v, ws, w, desc, reps: int = 20):
     return res
 
 
+def backward_lap(ra, q, kb, vb, out, lse, w, rank, mask, order, step_flops, laps):
+    """Time the backward lap: ra_bwd_init, one ra_bwd_block_step per block in ring order
+    (each block's dK, dV accumulating in its own buffer), ra_bwd_finalize.  Useful flops:
+    10*d per allowed pair (the five products of the standard backward: the recomputed scores,
+    dP, dV, dK, dQ); the kernels recompute the scores and dP once more for the dQ side."""
+    import torch
+    g = torch.Generator(device="cpu").manual_seed(1)
+    d_out = torch.randn(q.shape, generator=g).to(q.dtype).to(q.device)
+    dks = [torch.zeros(kb[j].shape, dtype=torch.float32, device=q.device) for j in range(w.P)]
+    dvs = [torch.zeros(vb[j].shape, dtype=torch.float32, device=q.device) for j in range(w.P)]
+    dq = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+    ws = torch.empty(ra.bwd_workspace_bytes(ra.desc_for(q, kb[0], w.P)), dtype=torch.uint8, device=q.device)
+
+    def one():
+        bw = ra.RingBackward(q, d_out, out, lse, kb[0], ring_size=w.P, workspace=ws)
+        for j in order:
+            qo, ko = ra.block_offsets(mask, rank, j, w.n_local, w.n_local)
+            bw.step(kb[j], vb[j], dks[j], dvs[j], mask, qo, ko)
+        bw.finalize(dq)
+        bw.close()
+
+    one()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(laps):
+        one()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / laps
+    flops = sum(step_flops) // 4 * 10      # 10*d per pair (step_flops holds 4*d per pair)
+    return {"ms_per_lap": round(ms, 4), "useful_flops_per_lap": flops,
+            "TFLOP_s": round(flops / ms / 1e9, 1), "pct_of_peak": round(flops / ms / 1e9 / PEAK_BF16_TFLOPS * 100, 2),
+            "flop_convention": "10*d per allowed pair per query head"}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -161,6 +197,8 @@ def main() -> int:
     ap.add_argument("--rank", type=int, default=None, help="measured rank (default: the workload's first)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="oracle timing budget")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--backward", action="store_true",
+                    help="also time the backward lap (ra_bwd_*) after the forward laps")
     ap.add_argument("--hbm-passes", action="store_true",
                     help="also time the HBM-bound passes (finalize, short KV blocks, state merge)")
     args = ap.parse_args()
@@ -256,6 +294,8 @@ def main() -> int:
     }
 
     hbm = hbm_passes(ra, qd, kb[0], vb[0], ws, w, desc) if args.hbm_passes else None
+    bwd = backward_lap(ra, qd, kb, vb, out, lse, w, rank, mask, order, step_flops, args.steps) \
+        if args.backward else None
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -298,6 +338,7 @@ def main() -> int:
             "torch": torch.__version__, "hip": torch.version.hip,
             "kernel_source_sha": kernel_source_sha(),
             "hbm_passes": hbm,
+            "backward": bwd,
         },
     }
     print(json.dumps(line), flush=True)

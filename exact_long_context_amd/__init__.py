@@ -96,6 +96,10 @@ def workspace_bytes(desc: ra_desc) -> int:
     return int(lib().ra_workspace_bytes(C.byref(desc)))
 
 
+def bwd_workspace_bytes(desc: ra_desc) -> int:
+    return lib().ra_bwd_workspace_bytes(C.byref(desc))
+
+
 def workspace_layout(desc: ra_desc) -> tuple[int, int, int]:
     o, m, l_ = C.c_size_t(), C.c_size_t(), C.c_size_t()
     check(lib().ra_workspace_layout(C.byref(desc), C.byref(o), C.byref(m), C.byref(l_)))

@@ -31,6 +31,7 @@ SOURCES = [
     "ra_finalize.hip",
     "ra_merge.hip",
     "ra_bwd.hip",
+    "ra_bwd_bf16.hip",
 ]
 
 ARCH = "gfx950"

@@ -511,8 +511,9 @@ int ra_bwd_block_step(ra_bwd* st, const void* k, const void* v, float* dk, float
     p.dkv_rows = kv_len;
     p.diag = b.diag;
     p.scale = d->softmax_scale;
-    hipError_t e = ra::launch_bwd_step_valu(p, d->head_dim, d->dtype == RA_DTYPE_BF16,
-                                            static_cast<hipStream_t>(d->stream));
+    hipStream_t stream = static_cast<hipStream_t>(d->stream);
+    hipError_t e = d->dtype == RA_DTYPE_BF16 ? ra::launch_bwd_step_bf16(p, d->head_dim, stream)
+                                             : ra::launch_bwd_step_f32(p, d->head_dim, stream);
     if (e != hipSuccess) return hip_fail(e, "backward step launch");
   }
   add_stats(&st->stats, &s);

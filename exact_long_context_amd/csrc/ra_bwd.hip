@@ -7,8 +7,9 @@
 //     D   = rowsum(dO * O),   dV += P^T dO,   dS = P * (dO V^T - D),
 //     dQ += scale * dS K,     dK += scale * dS^T Q.
 //
-// These are the vector-unit kernels (fp32 FMA; bf16 inputs are widened on load).  Each
-// output has one owner, so nothing is accumulated with atomics:
+// These are the fp32 kernels (vector-unit FMA, the exactness path; the bf16 path runs on the
+// matrix cores, ra_bwd_bf16.hip), plus the D pass shared by both.  Each output has one owner,
+// so nothing is accumulated with atomics:
 //  * bwd_dq_kernel: a workgroup owns 64 query rows of one head (four lanes per row, each
 //    with a quarter of the head dimension) and streams the block's keys through LDS;
 //  * bwd_dkdv_kernel: a workgroup owns 64 keys of one KV head and streams the query rows
@@ -241,9 +242,9 @@ hipError_t launch_bwd_prep(const BwdPrepParams& p, int head_dim, bool bf16, hipS
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_bwd_step_valu(const BwdParams& p, int head_dim, bool bf16, hipStream_t stream) {
-  if (head_dim == 64) return bf16 ? launch_all<__bf16, 64>(p, stream) : launch_all<float, 64>(p, stream);
-  if (head_dim == 128) return bf16 ? launch_all<__bf16, 128>(p, stream) : launch_all<float, 128>(p, stream);
+hipError_t launch_bwd_step_f32(const BwdParams& p, int head_dim, hipStream_t stream) {
+  if (head_dim == 64) return launch_all<float, 64>(p, stream);
+  if (head_dim == 128) return launch_all<float, 128>(p, stream);
   return hipErrorInvalidValue;
 }
 

@@ -1,0 +1,427 @@
+// ra_bwd_bf16.hip -- the backward ring step on the matrix cores (bf16 operands, fp32
+// accumulation), for the step that "Ring Attention：把超长序列沿设备环流动", section
+// Backward 需要让梯度也沿环传播 describes: dQ stays with the query owner, dK and dV accumulate
+// on the travelling block, probabilities are recomputed from the forward's saved logsumexp.
+// With P = exp(scale * <q, k> - lse) on allowed pairs:
+//     dV += P^T dO,   dS = P * (dO V^T - D),   dQ += scale * dS K,   dK += scale * dS^T Q.
+//
+// v_mfma_f32_32x32x16_bf16 throughout, with the operand layouts of the forward kernel (lane l
+// of operand A holds row l%32 and k = 8*(l/32)..+7; of B column l%32, same k; of the result
+// column l%32 and rows 8*(j/4) + 4*(l/32) + j%4):
+//  * bwd_dq_kernel (a workgroup of 4 waves owns 128 query rows of one head, 32 per wave):
+//      S^T = K Q^T and dP^T = V dO^T (K and V rows from LDS as A, q and dO resident as B),
+//      dS^T formed in registers and rounded to bf16, then dQ^T += K^T dS^T with K^T read by
+//      ds_read_b64_tr_b16 from the same LDS tile: the forward's P V product with K for V.
+//  * bwd_dkdv_kernel (a workgroup of 4 waves owns 128 keys of one KV head, 32 per wave, one
+//      wave per SIMD): S = Q K^T and dP = dO V^T (Q and dO rows from LDS as A, K and V
+//      resident as B), P and dS in registers, then dV^T += dO^T P and dK^T += Q^T dS with the
+//      transposed operands read by ds_read_b64_tr_b16; it walks the query rows of every query
+//      head that reads its KV head.
+// Streamed tiles are 32 rows, double-buffered, copied straight from HBM into LDS with
+// buffer_load ... lds; one XOR swizzle per tile serves the 16-byte operand reads (conflict
+// free) and the transposing reads (at most two-way conflicts).  Each output has one owner: no
+// atomics.  Only tiles holding an allowed pair are visited; the element mask runs on every
+// visited tile (cheap next to the five products).
+
+#include <hip/hip_runtime.h>
+
+#include <type_traits>
+
+#include "ra_internal.h"
+#include "ra_pos.h"
+
+namespace ra {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __attribute__((address_space(3))) void lds_void;
+
+constexpr int NT = 256;     // 4 waves
+constexpr int WR = 32;      // rows (dq) or keys (dkdv) per wave
+constexpr int BO = 4 * WR;  // owned per workgroup
+constexpr int BT = 32;      // streamed tile rows
+constexpr float kLog2e = 1.4426950408889634f;
+
+// physical 16-byte chunk of logical chunk c of tile row t
+template <int D>
+__device__ __forceinline__ int phys(int t, int c) {
+  if constexpr (D == 128) return c ^ (t & 15);
+  else return c ^ ((t >> 1) & 7);
+}
+
+__device__ __forceinline__ void load_lds_b128_bwd(__amdgpu_buffer_rsrc_t r, void* lds, int voff, int soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 16, voff, soff, 0, 0);
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_bwd(const void* base, int64_t bytes) {
+  const int n = bytes > 0x7fffffff ? 0x7fffffff : (int)(bytes < 0 ? 0 : bytes);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, 0x00020000);
+}
+
+template <int N>
+using ic = std::integral_constant<int, N>;
+
+// Per-lane pieces shared by both kernels: where this lane's 16-byte operand chunks sit in a
+// tile (k_roff: row r32, chunk 2*ks + hi) and where its transposing reads go (t_roff: rows
+// 4*(g>>1) + e (+8 for the second half, +16*kk as an immediate), columns 32*vb + 16*(g&1) +
+// 4*a), and which global chunk it fetches for each direct load.
+template <int D>
+struct TileMap {
+  static constexpr int KS = D / 16, VB = D / 32, RB = D * 2, CPR = D / 8, RPL = 64 / CPR;
+  static constexpr int LPW = BT * RB / 1024 / 4;
+  int k_roff[KS];
+  int t_roff[2][VB];
+  int goff[LPW];
+  __device__ void init(int lane, int wave, int row_bytes) {
+    const int r32 = lane & 31, hi = lane >> 5;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) k_roff[ks] = r32 * RB + (phys<D>(r32, 2 * ks + hi) << 4);
+    const int g = lane >> 4, a = lane & 3, e = (lane >> 2) & 3;
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const int row = 4 * (g >> 1) + e + 8 * half;
+#pragma unroll
+      for (int vb = 0; vb < VB; ++vb) {
+        const int dv = 32 * vb + 16 * (g & 1) + 4 * a;
+        t_roff[half][vb] = row * RB + (phys<D>(row, dv >> 3) << 4) + ((dv & 7) << 1);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < LPW; ++u) {
+      const int t = (wave * LPW + u) * RPL + lane / CPR;
+      goff[u] = (lane / CPR) * row_bytes + phys<D>(t, lane % CPR) * 16;
+    }
+  }
+  // one tile of BT rows starting at global row r0 of base (row stride row_bytes, rows valid)
+  __device__ void load(unsigned char* tile, const __bf16* base, int64_t r0, int64_t rows, int64_t st,
+                       int wave, int row_bytes) const {
+    const __amdgpu_buffer_rsrc_t r = rsrc_bwd(base + r0 * st, (rows - r0) * st * 2);
+#pragma unroll
+    for (int u = 0; u < LPW; ++u) {
+      const int row0 = (wave * LPW + u) * RPL;
+      load_lds_b128_bwd(r, tile + row0 * RB, goff[u], row0 * row_bytes);
+    }
+  }
+  __device__ bf16x8 rd(const unsigned char* tile, int ks) const {
+    return *reinterpret_cast<const bf16x8*>(tile + k_roff[ks]);
+  }
+  __device__ bf16x8 rd_t(const unsigned char* tile, int kk, int vb) const {
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(tile + t_roff[0][vb] + kk * 16 * RB));
+    const s16x4 hi8 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(tile + t_roff[1][vb] + kk * 16 * RB));
+    const s16x8 both = __builtin_shufflevector(lo, hi8, 0, 1, 2, 3, 4, 5, 6, 7);
+    bf16x8 x;
+    __builtin_memcpy(&x, &both, sizeof x);
+    return x;
+  }
+};
+
+__device__ __forceinline__ bf16x8 row_chunk(const __bf16* p, bool ok) {
+  bf16x8 x;
+  if (ok) {
+    x = *reinterpret_cast<const bf16x8*>(p);
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = (__bf16)0.0f;
+  }
+  return x;
+}
+
+// ------------------------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void bwd_dq_kernel(BwdParams p) {
+  using M = TileMap<D>;
+  constexpr int KS = M::KS, VB = M::VB, RB = M::RB;
+  __shared__ __attribute__((aligned(16))) unsigned char k_t0[BT * RB];
+  __shared__ __attribute__((aligned(16))) unsigned char k_t1[BT * RB];
+  __shared__ __attribute__((aligned(16))) unsigned char v_t0[BT * RB];
+  __shared__ __attribute__((aligned(16))) unsigned char v_t1[BT * RB];
+  unsigned char* const k_tiles[2] = {k_t0, k_t1};
+  unsigned char* const v_tiles[2] = {v_t0, v_t1};
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int r32 = lane & 31, hi = lane >> 5;
+  const int n_qt = (p.n_q + BO - 1) / BO;
+  const int total = gridDim.x;
+  int L = blockIdx.x;
+  if ((total & 7) == 0) L = (L & 7) * (total >> 3) + (L >> 3);
+  const int g_in = L % p.group;
+  L /= p.group;
+  const int qt = n_qt - 1 - (L % n_qt);
+  L /= n_qt;
+  const int g = L % p.kv_heads;
+  const int b = L / p.kv_heads;
+  const int h = g * p.group + g_in;
+  const int i0 = qt * BO, i1 = min(i0 + BO, p.n_q);
+  const int kt_live = tiles_live(i0, i1, p.diag, p.n_k, BT);
+  if (kt_live == 0) return;   // no allowed pair: dQ gets nothing from this block
+
+  const int row = i0 + wave * WR + r32;
+  const bool row_ok = row < p.n_q;
+  const int64_t srow = ((int64_t)b * p.q_heads + h) * p.state_rows + row;
+  const __bf16* qrow = static_cast<const __bf16*>(p.q) + (int64_t)b * p.q_sb + (int64_t)h * p.q_sh + (int64_t)row * p.q_st + hi * 8;
+  const __bf16* dorow = static_cast<const __bf16*>(p.d_out) + (int64_t)b * p.q_sb + (int64_t)h * p.q_sh + (int64_t)row * p.q_st + hi * 8;
+  bf16x8 qf[KS], dof[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    qf[ks] = row_chunk(qrow + ks * 16, row_ok);
+    dof[ks] = row_chunk(dorow + ks * 16, row_ok);
+  }
+  const float lse2 = row_ok ? p.lse[srow] * kLog2e : -INFINITY;
+  const float Dr = row_ok ? p.D[srow] : 0.f;
+  const float c2 = p.scale * kLog2e;
+
+  M map;
+  const int row_bytes = (int)(p.k_st * 2);
+  map.init(lane, wave, row_bytes);
+  const __bf16* kg = static_cast<const __bf16*>(p.k) + (int64_t)b * p.k_sb + (int64_t)g * p.k_sh;
+  const __bf16* vg = static_cast<const __bf16*>(p.v) + (int64_t)b * p.k_sb + (int64_t)g * p.k_sh;
+
+  f32x16 dq[VB];
+#pragma unroll
+  for (int vb = 0; vb < VB; ++vb)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) dq[vb][j] = 0.f;
+
+  auto step = [&](auto bufc, int kt) {
+    constexpr int B = decltype(bufc)::value;
+    // next tile into the other buffer (past the last live tile: zeros or unused keys)
+    map.load(k_tiles[1 - B], kg, (int64_t)(kt + 1) * BT, p.n_k, p.k_st, wave, row_bytes);
+    map.load(v_tiles[1 - B], vg, (int64_t)(kt + 1) * BT, p.n_k, p.k_st, wave, row_bytes);
+    const unsigned char* kt_b = k_tiles[B];
+    const unsigned char* vt_b = v_tiles[B];
+    f32x16 s, dp;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      s[j] = 0.f;
+      dp[j] = 0.f;
+    }
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(map.rd(kt_b, ks), qf[ks], s, 0, 0, 0);
+      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(map.rd(vt_b, ks), dof[ks], dp, 0, 0, 0);
+    }
+    // lane holds keys 8*(j/4) + 4*hi + (j%4) of this row
+    const int lim = min(row + p.diag, p.n_k - 1) - kt * BT - 4 * hi;
+    bf16x8 dsk[2];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const bool ok = (8 * (j >> 2) + (j & 3) <= lim) && lse2 != -INFINITY;
+      const float pr = ok ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[j], c2, -lse2)) : 0.f;
+      dsk[j >> 3][j & 7] = (__bf16)(pr * (dp[j] - Dr) * p.scale);
+    }
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int vb = 0; vb < VB; ++vb)
+        dq[vb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(map.rd_t(kt_b, kk, vb), dsk[kk], dq[vb], 0, 0, 0);
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's copies of the next tile
+    __syncthreads();
+  };
+
+  map.load(k_tiles[0], kg, 0, p.n_k, p.k_st, wave, row_bytes);
+  map.load(v_tiles[0], vg, 0, p.n_k, p.k_st, wave, row_bytes);
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+  __syncthreads();
+  for (int kt = 0; kt < kt_live; kt += 2) {
+    step(ic<0>{}, kt);
+    if (kt + 1 < kt_live) step(ic<1>{}, kt + 1);
+  }
+
+  if (row_ok) {
+    float* op = p.dq + srow * D + 4 * hi;
+#pragma unroll
+    for (int vb = 0; vb < VB; ++vb)
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        float4* q4 = reinterpret_cast<float4*>(op + vb * 32 + 8 * a);
+        float4 x = *q4;
+        x.x += dq[vb][4 * a + 0];
+        x.y += dq[vb][4 * a + 1];
+        x.z += dq[vb][4 * a + 2];
+        x.w += dq[vb][4 * a + 3];
+        *q4 = x;
+      }
+  }
+}
+
+// ------------------------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void bwd_dkdv_kernel(BwdParams p) {
+  using M = TileMap<D>;
+  constexpr int KS = M::KS, VB = M::VB, RB = M::RB;
+  __shared__ __attribute__((aligned(16))) unsigned char q_t0[BT * RB];
+  __shared__ __attribute__((aligned(16))) unsigned char q_t1[BT * RB];
+  __shared__ __attribute__((aligned(16))) unsigned char o_t0[BT * RB];
+  __shared__ __attribute__((aligned(16))) unsigned char o_t1[BT * RB];
+  __shared__ __attribute__((aligned(16))) float lse_t[2][BT];
+  __shared__ __attribute__((aligned(16))) float d_t[2][BT];
+  unsigned char* const q_tiles[2] = {q_t0, q_t1};
+  unsigned char* const o_tiles[2] = {o_t0, o_t1};
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int r32 = lane & 31, hi = lane >> 5;
+  const int n_kt = (p.n_k + BO - 1) / BO;
+  const int total = gridDim.x;
+  int L = blockIdx.x;
+  if ((total & 7) == 0) L = (L & 7) * (total >> 3) + (L >> 3);
+  const int kt = L % n_kt;
+  L /= n_kt;
+  const int g = L % p.kv_heads;
+  const int b = L / p.kv_heads;
+  const int t0 = kt * BO;
+  const int key = t0 + wave * WR + r32;
+  const bool key_ok = key < p.n_k;
+  // query rows that can see some key of this workgroup: i >= t0 - diag
+  const int i_first = max(0, t0 - p.diag);
+  if (i_first >= p.n_q) return;
+  const int r_start = (i_first / BT) * BT;
+  const int n_rt = (p.n_q - r_start + BT - 1) / BT;   // query tiles per head
+  const int n_it = n_rt * p.group;                     // over every head of the group
+
+  const __bf16* krow = static_cast<const __bf16*>(p.k) + (int64_t)b * p.k_sb + (int64_t)g * p.k_sh + (int64_t)key * p.k_st + hi * 8;
+  const __bf16* vrow = static_cast<const __bf16*>(p.v) + (int64_t)b * p.k_sb + (int64_t)g * p.k_sh + (int64_t)key * p.k_st + hi * 8;
+  bf16x8 kf[KS], vf[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    kf[ks] = row_chunk(krow + ks * 16, key_ok);
+    vf[ks] = row_chunk(vrow + ks * 16, key_ok);
+  }
+  const float c2 = p.scale * kLog2e;
+  M map;
+  const int row_bytes = (int)(p.q_st * 2);
+  map.init(lane, wave, row_bytes);
+
+  f32x16 dk[VB], dv[VB];
+#pragma unroll
+  for (int vb = 0; vb < VB; ++vb)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      dk[vb][j] = 0.f;
+      dv[vb][j] = 0.f;
+    }
+
+  // iteration u: head g*group + u / n_rt, query rows r_start + (u % n_rt) * BT ..
+  auto stage = [&](int buf, int u) {
+    const int hh = u / n_rt;
+    const int r0 = r_start + (u % n_rt) * BT;
+    const int h = g * p.group + (hh < p.group ? hh : p.group - 1);
+    const __bf16* qb = static_cast<const __bf16*>(p.q) + (int64_t)b * p.q_sb + (int64_t)h * p.q_sh;
+    const __bf16* ob = static_cast<const __bf16*>(p.d_out) + (int64_t)b * p.q_sb + (int64_t)h * p.q_sh;
+    map.load(q_tiles[buf], qb, r0, p.n_q, p.q_st, wave, row_bytes);
+    map.load(o_tiles[buf], ob, r0, p.n_q, p.q_st, wave, row_bytes);
+    if (tid < BT) {
+      const int i = r0 + tid;
+      const bool ok = hh < p.group && i < p.n_q;
+      const int64_t sr = ((int64_t)b * p.q_heads + h) * p.state_rows + i;
+      lse_t[buf][tid] = ok ? p.lse[sr] * kLog2e : -INFINITY;
+      d_t[buf][tid] = ok ? p.D[sr] : 0.f;
+    }
+  };
+
+  auto step = [&](auto bufc, int u) {
+    constexpr int B = decltype(bufc)::value;
+    stage(1 - B, u + 1);   // the next tile (past the last: a clamped head, rows masked out)
+    const int r0 = r_start + (u % n_rt) * BT;
+    const unsigned char* qt_b = q_tiles[B];
+    const unsigned char* ot_b = o_tiles[B];
+    f32x16 s, dp;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      s[j] = 0.f;
+      dp[j] = 0.f;
+    }
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(map.rd(qt_b, ks), kf[ks], s, 0, 0, 0);
+      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(map.rd(ot_b, ks), vf[ks], dp, 0, 0, 0);
+    }
+    // lane holds key `key` against tile rows 8*(j/4) + 4*hi + (j%4)
+    const float4* lse4 = reinterpret_cast<const float4*>(&lse_t[B][0]);
+    const float4* d4 = reinterpret_cast<const float4*>(&d_t[B][0]);
+    bf16x8 pb[2], dsb[2];
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      const float4 l4 = lse4[2 * a + hi];   // rows 8a + 4hi .. +3
+      const float4 dd = d4[2 * a + hi];
+      const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+      const float dvv[4] = {dd.x, dd.y, dd.z, dd.w};
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int j = 4 * a + c;
+        const int i = r0 + 8 * a + 4 * hi + c;
+        const bool ok = key_ok && i < p.n_q && key <= i + p.diag && lv[c] != -INFINITY;
+        const float pr = ok ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[j], c2, -lv[c])) : 0.f;
+        pb[j >> 3][j & 7] = (__bf16)pr;
+        dsb[j >> 3][j & 7] = (__bf16)(pr * (dp[j] - dvv[c]) * p.scale);
+      }
+    }
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int vb = 0; vb < VB; ++vb) {
+        dv[vb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(map.rd_t(ot_b, kk, vb), pb[kk], dv[vb], 0, 0, 0);
+        dk[vb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(map.rd_t(qt_b, kk, vb), dsb[kk], dk[vb], 0, 0, 0);
+      }
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __syncthreads();
+  };
+
+  stage(0, 0);
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+  __syncthreads();
+  for (int u = 0; u < n_it; u += 2) {
+    step(ic<0>{}, u);
+    if (u + 1 < n_it) step(ic<1>{}, u + 1);
+  }
+
+  if (key_ok) {
+    const int64_t kbase = (((int64_t)b * p.kv_heads + g) * p.dkv_rows + key) * D + 4 * hi;
+#pragma unroll
+    for (int vb = 0; vb < VB; ++vb)
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        float4* k4 = reinterpret_cast<float4*>(p.dk + kbase + vb * 32 + 8 * a);
+        float4* v4 = reinterpret_cast<float4*>(p.dv + kbase + vb * 32 + 8 * a);
+        float4 x = *k4, y = *v4;
+        x.x += dk[vb][4 * a + 0];
+        x.y += dk[vb][4 * a + 1];
+        x.z += dk[vb][4 * a + 2];
+        x.w += dk[vb][4 * a + 3];
+        y.x += dv[vb][4 * a + 0];
+        y.y += dv[vb][4 * a + 1];
+        y.z += dv[vb][4 * a + 2];
+        y.w += dv[vb][4 * a + 3];
+        *k4 = x;
+        *v4 = y;
+      }
+  }
+}
+
+template <int D>
+hipError_t launch_d(const BwdParams& p, hipStream_t stream) {
+  const int64_t gq = (int64_t)((p.n_q + BO - 1) / BO) * p.q_heads * p.batch;
+  const int64_t gk = (int64_t)((p.n_k + BO - 1) / BO) * p.kv_heads * p.batch;
+  if (gq > 0) hipLaunchKernelGGL((bwd_dq_kernel<D>), dim3((unsigned)gq), dim3(NT), 0, stream, p);
+  if (gk > 0) hipLaunchKernelGGL((bwd_dkdv_kernel<D>), dim3((unsigned)gk), dim3(NT), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_bwd_step_bf16(const BwdParams& p, int head_dim, hipStream_t stream) {
+  switch (head_dim) {
+    case 64: return launch_d<64>(p, stream);
+    case 128: return launch_d<128>(p, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace ra

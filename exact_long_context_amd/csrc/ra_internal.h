@@ -97,6 +97,7 @@ hipError_t launch_step_f32(const StepParams& p, int head_dim, hipStream_t stream
 hipError_t launch_finalize(const FinalizeParams& p, hipStream_t stream);
 hipError_t launch_merge(const MergeParams& p, hipStream_t stream);
 hipError_t launch_bwd_prep(const BwdPrepParams& p, int head_dim, bool bf16, hipStream_t stream);
-hipError_t launch_bwd_step_valu(const BwdParams& p, int head_dim, bool bf16, hipStream_t stream);
+hipError_t launch_bwd_step_f32(const BwdParams& p, int head_dim, hipStream_t stream);
+hipError_t launch_bwd_step_bf16(const BwdParams& p, int head_dim, hipStream_t stream);
 
 }  // namespace ra

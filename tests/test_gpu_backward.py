@@ -113,3 +113,53 @@ def test_backward_rows_without_keys_and_accumulation():
     assert torch.equal(dk, carried) and torch.equal(dv, carried)
     assert not dq.any()
     bw.close()
+
+
+def test_backward_full_size_sampled_rows_and_keys():
+    """The 16K x 16K causal diagonal block at full size (rank 0 of the 131072-token,
+    8-rank contiguous ring, 32 heads): sampled dQ rows and sampled keys of dK, dV against the
+    oracle, whose forward for head 0 (lse, O) it computes itself."""
+    import exact_long_context_amd as ra
+    from exact_long_context_amd.workload import shard_blocks
+    from gpu_util import seeded_rows
+    w = synth.WORKLOADS["causal_contig_n131072_p8_h32"]
+    rank = 0
+    say(f"  generating {w.name} rank {rank}")
+    q, k, v = synth.workload_tensors(w, rank)
+    n = w.n_local
+    d_out = synth.random_case(9, 1, w.q_heads, 1, n, 1, w.head_dim, "bf16")[0]
+    kb, vb = shard_blocks(k.cuda(), v.cuda(), w.P, w.layout)
+    qd, dod = q.cuda(), d_out.cuda()
+    ring = ra.EmulatedRing(kb, vb)
+    o, lse, _ = ring.lap(qd, rank, CONTIG)
+    bw = ra.RingBackward(qd, dod, o, lse, kb[0], ring_size=w.P)
+    dk0 = torch.zeros(kb[0].shape, dtype=torch.float32, device="cuda")
+    dv0 = torch.zeros_like(dk0)
+    scratch_k = torch.zeros_like(dk0)
+    scratch_v = torch.zeros_like(dk0)
+    for j in oracle.ring_visit_order(w.P, rank):
+        qo, ko = ra.block_offsets(CONTIG, rank, j, n, n)
+        bw.step(kb[j], vb[j], dk0 if j == 0 else scratch_k, dv0 if j == 0 else scratch_v, CONTIG, qo, ko)
+    dq = bw.finalize()
+    assert bw.stats()["blocks_skipped"] == w.P - 1
+    bw.close()
+    torch.cuda.synchronize()
+    assert not scratch_k.any() and not scratch_v.any()   # every other block is in the future
+    # oracle, head 0: rank 0's rows against block 0 (the only keys they may see)
+    q_pos = np.arange(n)
+    q64 = to64(q[:, :1])
+    k64 = to64(k[:, :1, :n])
+    v64 = to64(v[:, :1, :n])
+    do64 = to64(d_out[:, :1])
+    say("  oracle forward, head 0")
+    o_ref, lse_ref = oracle.dense_attention(q64, k64, v64, q_pos, q_pos, True)
+    D = oracle.backward_row_terms(do64, o_ref)
+    rows = seeded_rows(n, 48, 3)
+    gq, _, _ = oracle.backward_block(q64[:, :, rows], k64, v64, do64[:, :, rows], lse_ref[:, :, rows],
+                                     D[:, :, rows], q_pos[rows], q_pos, True)
+    assert_bf16_close(to64(dq[:, :1, rows]), gq, "dQ sampled rows")
+    keys = seeded_rows(n, 48, 4)
+    _, gk, gv = oracle.backward_block(q64, k64[:, :, keys], v64[:, :, keys], do64, lse_ref, D, q_pos,
+                                      q_pos[keys], True)
+    assert_bf16_close(to64(dk0[:, :1, keys]), gk, "dK sampled keys")
+    assert_bf16_close(to64(dv0[:, :1, keys]), gv, "dV sampled keys")
