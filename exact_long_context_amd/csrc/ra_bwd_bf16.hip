@@ -12,11 +12,14 @@
 //      S^T = K Q^T and dP^T = V dO^T (K and V rows from LDS as A, q and dO resident as B),
 //      dS^T formed in registers and rounded to bf16, then dQ^T += K^T dS^T with K^T read by
 //      ds_read_b64_tr_b16 from the same LDS tile: the forward's P V product with K for V.
-//  * bwd_dkdv_kernel (a workgroup of 4 waves owns 128 keys of one KV head, 32 per wave, one
-//      wave per SIMD): S = Q K^T and dP = dO V^T (Q and dO rows from LDS as A, K and V
-//      resident as B), P and dS in registers, then dV^T += dO^T P and dK^T += Q^T dS with the
-//      transposed operands read by ds_read_b64_tr_b16; it walks the query rows of every query
-//      head that reads its KV head.
+//  * bwd_kv_kernel (a workgroup of 4 waves owns the keys of one KV head: for dV 64 per wave as
+//      two halves, one wave per SIMD; for dK 32 per wave, two waves per SIMD, since it also
+//      holds V resident), in two modes launched one after the other: MODE_DV forms
+//      S = Q K^T and P, then dV^T += dO^T P; MODE_DK forms S and dP = dO V^T, then dS, then
+//      dK^T += Q^T dS (Q and dO rows from LDS as A, K and V resident as B, the transposed
+//      operands by ds_read_b64_tr_b16).  Each walks the query rows of every query head that
+//      reads its KV head.  Splitting dV from dK recomputes the scores once more but halves
+//      the streamed operand bytes per matrix instruction.
 // Streamed tiles are 32 rows, double-buffered, copied straight from HBM into LDS with
 // buffer_load ... lds; one XOR swizzle per tile serves the 16-byte operand reads (conflict
 // free) and the transposing reads (at most two-way conflicts).  Each output has one owner: no
@@ -251,11 +254,27 @@ void bwd_dq_kernel(BwdParams p) {
 }
 
 // ------------------------------------------------------------------------------------------
-template <int D>
-__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void bwd_dkdv_kernel(BwdParams p) {
+// Key-stationary kernels: a workgroup of 4 waves owns 128 * KH keys of one KV head, 32 * KH
+// per wave (with two halves each streamed operand read feeds both).
+// MODE_DV forms P and accumulates dV^T += dO^T P; MODE_DK forms P and dP, then dS, and
+// accumulates dK^T += Q^T dS.  Both recompute the scores; keeping them apart holds each one's
+// registers and LDS traffic per matrix instruction at the forward kernel's level.
+constexpr int MODE_DV = 0, MODE_DK = 1;
+// 32-key halves per wave.  Two halves (one wave per SIMD) halve the streamed operand bytes
+// per matrix instruction but leave one wave to hide every latency; measured, one half at two
+// waves per SIMD is faster for both modes (dV 10.4 ms -> see the design notes).
+template <int MODE>
+constexpr int kv_halves() { return 1; }
+
+template <int D, int MODE>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(3 - kv_halves<MODE>(), 3 - kv_halves<MODE>())))
+void bwd_kv_kernel(BwdParams p) {
+  constexpr int KH = kv_halves<MODE>();
+  constexpr int KW = 32 * KH;   // keys per wave
+  constexpr int KO = 4 * KW;    // keys per workgroup
   using M = TileMap<D>;
   constexpr int KS = M::KS, VB = M::VB, RB = M::RB;
+  constexpr bool DK = MODE == MODE_DK;
   __shared__ __attribute__((aligned(16))) unsigned char q_t0[BT * RB];
   __shared__ __attribute__((aligned(16))) unsigned char q_t1[BT * RB];
   __shared__ __attribute__((aligned(16))) unsigned char o_t0[BT * RB];
@@ -268,7 +287,7 @@ void bwd_dkdv_kernel(BwdParams p) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r32 = lane & 31, hi = lane >> 5;
-  const int n_kt = (p.n_k + BO - 1) / BO;
+  const int n_kt = (p.n_k + KO - 1) / KO;
   const int total = gridDim.x;
   int L = blockIdx.x;
   if ((total & 7) == 0) L = (L & 7) * (total >> 3) + (L >> 3);
@@ -276,9 +295,7 @@ void bwd_dkdv_kernel(BwdParams p) {
   L /= n_kt;
   const int g = L % p.kv_heads;
   const int b = L / p.kv_heads;
-  const int t0 = kt * BO;
-  const int key = t0 + wave * WR + r32;
-  const bool key_ok = key < p.n_k;
+  const int t0 = kt * KO;
   // query rows that can see some key of this workgroup: i >= t0 - diag
   const int i_first = max(0, t0 - p.diag);
   if (i_first >= p.n_q) return;
@@ -286,27 +303,33 @@ void bwd_dkdv_kernel(BwdParams p) {
   const int n_rt = (p.n_q - r_start + BT - 1) / BT;   // query tiles per head
   const int n_it = n_rt * p.group;                     // over every head of the group
 
-  const __bf16* krow = static_cast<const __bf16*>(p.k) + (int64_t)b * p.k_sb + (int64_t)g * p.k_sh + (int64_t)key * p.k_st + hi * 8;
-  const __bf16* vrow = static_cast<const __bf16*>(p.v) + (int64_t)b * p.k_sb + (int64_t)g * p.k_sh + (int64_t)key * p.k_st + hi * 8;
-  bf16x8 kf[KS], vf[KS];
+  int key[KH];
+  bool key_ok[KH];
+  bf16x8 kf[KH][KS], vf[KH][DK ? KS : 1];
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    kf[ks] = row_chunk(krow + ks * 16, key_ok);
-    vf[ks] = row_chunk(vrow + ks * 16, key_ok);
+  for (int kh = 0; kh < KH; ++kh) {
+    key[kh] = t0 + wave * KW + kh * 32 + r32;
+    key_ok[kh] = key[kh] < p.n_k;
+    const __bf16* krow = static_cast<const __bf16*>(p.k) + (int64_t)b * p.k_sb + (int64_t)g * p.k_sh + (int64_t)key[kh] * p.k_st + hi * 8;
+    const __bf16* vrow = static_cast<const __bf16*>(p.v) + (int64_t)b * p.k_sb + (int64_t)g * p.k_sh + (int64_t)key[kh] * p.k_st + hi * 8;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      kf[kh][ks] = row_chunk(krow + ks * 16, key_ok[kh]);
+      if constexpr (DK) vf[kh][ks] = row_chunk(vrow + ks * 16, key_ok[kh]);
+    }
   }
   const float c2 = p.scale * kLog2e;
   M map;
   const int row_bytes = (int)(p.q_st * 2);
   map.init(lane, wave, row_bytes);
 
-  f32x16 dk[VB], dv[VB];
+  f32x16 acc[KH][VB];
 #pragma unroll
-  for (int vb = 0; vb < VB; ++vb)
+  for (int kh = 0; kh < KH; ++kh)
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      dk[vb][j] = 0.f;
-      dv[vb][j] = 0.f;
-    }
+    for (int vb = 0; vb < VB; ++vb)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) acc[kh][vb][j] = 0.f;
 
   // iteration u: head g*group + u / n_rt, query rows r_start + (u % n_rt) * BT ..
   auto stage = [&](int buf, int u) {
@@ -322,7 +345,7 @@ void bwd_dkdv_kernel(BwdParams p) {
       const bool ok = hh < p.group && i < p.n_q;
       const int64_t sr = ((int64_t)b * p.q_heads + h) * p.state_rows + i;
       lse_t[buf][tid] = ok ? p.lse[sr] * kLog2e : -INFINITY;
-      d_t[buf][tid] = ok ? p.D[sr] : 0.f;
+      if constexpr (DK) d_t[buf][tid] = ok ? p.D[sr] : 0.f;
     }
   };
 
@@ -332,43 +355,65 @@ void bwd_dkdv_kernel(BwdParams p) {
     const int r0 = r_start + (u % n_rt) * BT;
     const unsigned char* qt_b = q_tiles[B];
     const unsigned char* ot_b = o_tiles[B];
-    f32x16 s, dp;
+    f32x16 s[KH], dp[KH];
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      s[j] = 0.f;
-      dp[j] = 0.f;
-    }
+    for (int kh = 0; kh < KH; ++kh)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        s[kh][j] = 0.f;
+        dp[kh][j] = 0.f;
+      }
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(map.rd(qt_b, ks), kf[ks], s, 0, 0, 0);
-      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(map.rd(ot_b, ks), vf[ks], dp, 0, 0, 0);
+      const bf16x8 qa = map.rd(qt_b, ks);
+#pragma unroll
+      for (int kh = 0; kh < KH; ++kh) s[kh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[kh][ks], s[kh], 0, 0, 0);
+      if constexpr (DK) {
+        const bf16x8 oa = map.rd(ot_b, ks);
+#pragma unroll
+        for (int kh = 0; kh < KH; ++kh) dp[kh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa, vf[kh][ks], dp[kh], 0, 0, 0);
+      }
     }
-    // lane holds key `key` against tile rows 8*(j/4) + 4*hi + (j%4)
+    // lane holds key key[kh] against tile rows 8*(j/4) + 4*hi + (j%4)
     const float4* lse4 = reinterpret_cast<const float4*>(&lse_t[B][0]);
     const float4* d4 = reinterpret_cast<const float4*>(&d_t[B][0]);
-    bf16x8 pb[2], dsb[2];
+    bf16x8 wb[KH][2];   // P (MODE_DV) or dS (MODE_DK) in bf16, per key half and 16-row step
 #pragma unroll
     for (int a = 0; a < 4; ++a) {
       const float4 l4 = lse4[2 * a + hi];   // rows 8a + 4hi .. +3
-      const float4 dd = d4[2 * a + hi];
       const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
-      const float dvv[4] = {dd.x, dd.y, dd.z, dd.w};
+      float dvv[4] = {0.f, 0.f, 0.f, 0.f};
+      if constexpr (DK) {
+        const float4 dd = d4[2 * a + hi];
+        dvv[0] = dd.x;
+        dvv[1] = dd.y;
+        dvv[2] = dd.z;
+        dvv[3] = dd.w;
+      }
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         const int j = 4 * a + c;
         const int i = r0 + 8 * a + 4 * hi + c;
-        const bool ok = key_ok && i < p.n_q && key <= i + p.diag && lv[c] != -INFINITY;
-        const float pr = ok ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[j], c2, -lv[c])) : 0.f;
-        pb[j >> 3][j & 7] = (__bf16)pr;
-        dsb[j >> 3][j & 7] = (__bf16)(pr * (dp[j] - dvv[c]) * p.scale);
+#pragma unroll
+        for (int kh = 0; kh < KH; ++kh) {
+          const bool ok = key_ok[kh] && i < p.n_q && key[kh] <= i + p.diag && lv[c] != -INFINITY;
+          const float pr = ok ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[kh][j], c2, -lv[c])) : 0.f;
+          if constexpr (DK)
+            wb[kh][j >> 3][j & 7] = (__bf16)(pr * (dp[kh][j] - dvv[c]) * p.scale);
+          else
+            wb[kh][j >> 3][j & 7] = (__bf16)pr;
+        }
       }
     }
+    const unsigned char* tr_tile = DK ? qt_b : ot_b;   // dK: Q^T dS; dV: dO^T P
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
       for (int vb = 0; vb < VB; ++vb) {
-        dv[vb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(map.rd_t(ot_b, kk, vb), pb[kk], dv[vb], 0, 0, 0);
-        dk[vb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(map.rd_t(qt_b, kk, vb), dsb[kk], dk[vb], 0, 0, 0);
+        const bf16x8 ta = map.rd_t(tr_tile, kk, vb);
+#pragma unroll
+        for (int kh = 0; kh < KH; ++kh)
+          acc[kh][vb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta, wb[kh][kk], acc[kh][vb], 0, 0, 0);
       }
     __builtin_amdgcn_s_waitcnt(0x0F70);
     __syncthreads();
@@ -382,25 +427,22 @@ void bwd_dkdv_kernel(BwdParams p) {
     if (u + 1 < n_it) step(ic<1>{}, u + 1);
   }
 
-  if (key_ok) {
-    const int64_t kbase = (((int64_t)b * p.kv_heads + g) * p.dkv_rows + key) * D + 4 * hi;
+  float* const out = DK ? p.dk : p.dv;
+#pragma unroll
+  for (int kh = 0; kh < KH; ++kh) {
+    if (!key_ok[kh]) continue;
+    const int64_t kbase = (((int64_t)b * p.kv_heads + g) * p.dkv_rows + key[kh]) * D + 4 * hi;
 #pragma unroll
     for (int vb = 0; vb < VB; ++vb)
 #pragma unroll
       for (int a = 0; a < 4; ++a) {
-        float4* k4 = reinterpret_cast<float4*>(p.dk + kbase + vb * 32 + 8 * a);
-        float4* v4 = reinterpret_cast<float4*>(p.dv + kbase + vb * 32 + 8 * a);
-        float4 x = *k4, y = *v4;
-        x.x += dk[vb][4 * a + 0];
-        x.y += dk[vb][4 * a + 1];
-        x.z += dk[vb][4 * a + 2];
-        x.w += dk[vb][4 * a + 3];
-        y.x += dv[vb][4 * a + 0];
-        y.y += dv[vb][4 * a + 1];
-        y.z += dv[vb][4 * a + 2];
-        y.w += dv[vb][4 * a + 3];
-        *k4 = x;
-        *v4 = y;
+        float4* o4 = reinterpret_cast<float4*>(out + kbase + vb * 32 + 8 * a);
+        float4 x = *o4;
+        x.x += acc[kh][vb][4 * a + 0];
+        x.y += acc[kh][vb][4 * a + 1];
+        x.z += acc[kh][vb][4 * a + 2];
+        x.w += acc[kh][vb][4 * a + 3];
+        *o4 = x;
       }
   }
 }
@@ -408,9 +450,11 @@ void bwd_dkdv_kernel(BwdParams p) {
 template <int D>
 hipError_t launch_d(const BwdParams& p, hipStream_t stream) {
   const int64_t gq = (int64_t)((p.n_q + BO - 1) / BO) * p.q_heads * p.batch;
-  const int64_t gk = (int64_t)((p.n_k + BO - 1) / BO) * p.kv_heads * p.batch;
+  const int64_t gv = (int64_t)((p.n_k + 128 * kv_halves<MODE_DV>() - 1) / (128 * kv_halves<MODE_DV>())) * p.kv_heads * p.batch;
+  const int64_t gk = (int64_t)((p.n_k + 128 * kv_halves<MODE_DK>() - 1) / (128 * kv_halves<MODE_DK>())) * p.kv_heads * p.batch;
   if (gq > 0) hipLaunchKernelGGL((bwd_dq_kernel<D>), dim3((unsigned)gq), dim3(NT), 0, stream, p);
-  if (gk > 0) hipLaunchKernelGGL((bwd_dkdv_kernel<D>), dim3((unsigned)gk), dim3(NT), 0, stream, p);
+  if (gv > 0) hipLaunchKernelGGL((bwd_kv_kernel<D, MODE_DV>), dim3((unsigned)gv), dim3(NT), 0, stream, p);
+  if (gk > 0) hipLaunchKernelGGL((bwd_kv_kernel<D, MODE_DK>), dim3((unsigned)gk), dim3(NT), 0, stream, p);
   return hipGetLastError();
 }
 
