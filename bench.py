@@ -20,6 +20,7 @@ from __future__ import annotations
 import argparse
 import hashlib
 import json
+import math
 import os
 import sys
 import time
@@ -152,6 +153,51 @@ def hbm_passes(ra, q, k, v, ws, w, desc, reps: int = 20):
     return res
 
 
+def decode_passes(ra, reps: int = 20):
+    """The split-KV block step (ra_decode_step) for few query rows of the long-context GQA
+    head shape (64 query heads over 8 KV heads, d = 128, bf16): one block of n_k keys per call
+    into a resumed state, for blocks from one ring block (16K keys) to the whole 1M-token
+    context.  Timed with events on the current stream over `reps` calls, beside the tiled
+    ra_block_step on the same block.  Bytes are algorithmic: K and V once, Q, the state read
+    and written, and the chunk states written and read back."""
+    import torch
+    import synth
+    B, Hq, Hkv, d = 1, 64, 8, 128
+    res = {}
+
+    def timed(fn):
+        fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    for n_q in (1, 8):
+        q = synth.draw_device(5, synth.Q_ID, 0, B, Hq, n_q, d, 1 / math.sqrt(128), "bf16", "cuda")
+        for nk in (16384, 131072, 1048576):
+            k = synth.draw_device(5, synth.K_ID, -1, B, Hkv, nk, d, 1 / math.sqrt(128), "bf16", "cuda")
+            v = synth.draw_device(5, synth.V_ID, -1, B, Hkv, nk, d, 1 / math.sqrt(128), "bf16", "cuda")
+            st = ra.RingState(q, k)
+            ws = torch.empty(ra.decode_workspace_bytes(st.desc, nk), dtype=torch.uint8, device="cuda")
+            st.decode_step(k, v, 0, workspace=ws)      # the state now holds a valid lap state
+            ms = timed(lambda: st.decode_step(k, v, 0, workspace=ws))
+            ms_tiled = timed(lambda: st.step(k, v, 0))
+            st.close()
+            rows = B * Hq * n_q
+            kv_bytes = 2 * B * Hkv * nk * d * 2
+            parts = ws.numel() // (rows * (d + 2) * 4) if rows else 0
+            nbytes = kv_bytes + rows * d * 2 + 2 * rows * (d + 2) * 4 + 2 * parts * rows * (d + 2) * 4
+            res[f"decode_q{n_q}_nk{nk}"] = {
+                "ms": round(ms, 4), "bytes": nbytes, "GB_s": round(nbytes / ms / 1e6, 1),
+                "frac_of_8TB_s": round(nbytes / ms / 1e6 / PEAK_HBM_GBS, 3),
+                "tiled_step_ms": round(ms_tiled, 4), "speedup_vs_tiled": round(ms_tiled / ms, 2)}
+            del k, v, ws
+    return res
+
+
 def backward_lap(ra, q, kb, vb, out, lse, w, rank, mask, order, step_flops, laps):
     """Time the backward lap: ra_bwd_init, one ra_bwd_block_step per block in ring order
     (each block's dK, dV accumulating in its own buffer), ra_bwd_finalize.  Useful flops:
@@ -199,6 +245,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--backward", action="store_true",
                     help="also time the backward lap (ra_bwd_*) after the forward laps")
+    ap.add_argument("--decode", action="store_true",
+                    help="also time the split-KV step for few query rows (decode) against 16K..1M keys")
     ap.add_argument("--hbm-passes", action="store_true",
                     help="also time the HBM-bound passes (finalize, short KV blocks, state merge)")
     args = ap.parse_args()
@@ -296,6 +344,7 @@ def main() -> int:
     hbm = hbm_passes(ra, qd, kb[0], vb[0], ws, w, desc) if args.hbm_passes else None
     bwd = backward_lap(ra, qd, kb, vb, out, lse, w, rank, mask, order, step_flops, args.steps) \
         if args.backward else None
+    dec = decode_passes(ra) if args.decode else None
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -339,6 +388,7 @@ def main() -> int:
             "kernel_source_sha": kernel_source_sha(),
             "hbm_passes": hbm,
             "backward": bwd,
+            "decode": dec,
         },
     }
     print(json.dumps(line), flush=True)

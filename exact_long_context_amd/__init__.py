@@ -96,6 +96,10 @@ def workspace_bytes(desc: ra_desc) -> int:
     return int(lib().ra_workspace_bytes(C.byref(desc)))
 
 
+def decode_workspace_bytes(desc: ra_desc, kv_len: int) -> int:
+    return int(lib().ra_decode_workspace_bytes(C.byref(desc), kv_len))
+
+
 def bwd_workspace_bytes(desc: ra_desc) -> int:
     return lib().ra_bwd_workspace_bytes(C.byref(desc))
 
@@ -163,6 +167,21 @@ class RingState:
             raise ValueError("K and V must have the strides the state was created for")
         check(lib().ra_block_step(self._handle(), k.data_ptr(), v.data_ptr(), k.shape[2], mask_kind,
                                   q_offset, k_offset))
+
+    def decode_step(self, k, v, mask_kind: int, q_offset: int = 0, k_offset: int = 0,
+                    workspace=None) -> None:
+        """ra_decode_step: the split-KV form of step() for a few query rows.  ``workspace`` is a
+        torch uint8 device tensor of at least decode_workspace_bytes(desc, k.shape[2]) bytes,
+        allocated here if not given."""
+        import torch
+        if k.stride() != v.stride() or tuple(k.stride()[:3]) != tuple(self.desc.kv_strides):
+            raise ValueError("K and V must have the strides the state was created for")
+        if workspace is None:
+            nbytes = decode_workspace_bytes(self.desc, k.shape[2])
+            workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=self.q.device)
+        check(lib().ra_decode_step(self._handle(), k.data_ptr(), v.data_ptr(), k.shape[2], mask_kind,
+                                   q_offset, k_offset, workspace.data_ptr(),
+                                   workspace.numel() * workspace.element_size()))
 
     def finalize(self, out=None, lse=None, want_lse: bool = True):
         import torch

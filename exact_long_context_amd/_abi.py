@@ -91,6 +91,9 @@ SIGNATURES = {
     "ra_block_step": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_int32, C.c_int32,
                                 C.c_int64, C.c_int64]),
     "ra_finalize": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p]),
+    "ra_decode_workspace_bytes": (C.c_size_t, [C.POINTER(ra_desc), C.c_int32]),
+    "ra_decode_step": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_int32, C.c_int32,
+                                 C.c_int64, C.c_int64, C.c_void_p, C.c_size_t]),
     "ra_bwd_workspace_bytes": (C.c_size_t, [C.POINTER(ra_desc)]),
     "ra_bwd_init": (C.c_int, [C.POINTER(ra_desc), C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
                               C.c_void_p, C.POINTER(C.c_void_p)]),

@@ -30,6 +30,7 @@ SOURCES = [
     "ra_step_f32.hip",
     "ra_finalize.hip",
     "ra_merge.hip",
+    "ra_decode.hip",
     "ra_bwd.hip",
     "ra_bwd_bf16.hip",
 ]

@@ -112,6 +112,12 @@ Layout layout_of(const ra_desc* d) {
   return L;
 }
 
+// A single token's stride never moves a pointer, but the kernels bound their buffer reads by
+// tokens x stride bytes, so a lone row is reported with at least a full row's stride.
+int64_t token_stride(int64_t stride, int32_t tokens, int32_t head_dim) {
+  return tokens <= 1 && stride < head_dim ? head_dim : stride;
+}
+
 int32_t pos_stride(int32_t mask_kind, const ra_desc* d) {
   return mask_kind == RA_MASK_CAUSAL_STRIPED ? d->ring_size : 1;
 }
@@ -239,6 +245,55 @@ int make_state(const ra_desc* d, const void* q, void* ws, int fresh, ra_state** 
   return RA_OK;
 }
 
+// The split-KV step: enough key chunks that the whole chip streams the block (about two
+// waves per SIMD of 256 compute units), none shorter than kDecodeMinChunk keys so that a
+// wave's fixed cost stays small next to its loads.
+constexpr int64_t kDecodeTargetWaves = 2048;
+constexpr int32_t kDecodeMinChunk = 256;
+
+struct DecodePlan {
+  int32_t n_parts, chunk;
+};
+
+int64_t decode_row_groups(const ra_desc* d) {
+  const int64_t packed = (int64_t)(d->q_heads / d->kv_heads) * d->q_len;
+  return (packed + ra::kDecodeRows - 1) / ra::kDecodeRows;
+}
+
+DecodePlan decode_plan(const ra_desc* d, int32_t n_keys) {
+  DecodePlan pl{0, 0};
+  if (n_keys <= 0) return pl;
+  const int64_t base = (int64_t)d->batch * d->kv_heads * decode_row_groups(d);
+  const int64_t want = base >= kDecodeTargetWaves ? 1 : (kDecodeTargetWaves + base - 1) / base;
+  int64_t chunk = (n_keys + want - 1) / want;
+  chunk = (chunk + ra::kDecodeTileK - 1) / ra::kDecodeTileK * ra::kDecodeTileK;
+  if (chunk < kDecodeMinChunk) chunk = kDecodeMinChunk;
+  pl.chunk = (int32_t)chunk;
+  pl.n_parts = (int32_t)((n_keys + chunk - 1) / chunk);
+  return pl;
+}
+
+struct DecodeLayout {
+  size_t o_off, m_off, l_off, total;
+};
+
+// Parts of a block of kv_len keys are at most decode_plan(kv_len)'s: a causal block only
+// ever plans over fewer keys, and fewer keys never give more parts (n_parts <= want and
+// n_parts <= ceil(keys / kDecodeMinChunk), both bounds non-decreasing in the key count).
+DecodeLayout decode_layout(const ra_desc* d, int32_t kv_len) {
+  const int64_t base = (int64_t)d->batch * d->kv_heads * decode_row_groups(d);
+  const int64_t want = base >= kDecodeTargetWaves ? 1 : (kDecodeTargetWaves + base - 1) / base;
+  int64_t parts = ((int64_t)kv_len + kDecodeMinChunk - 1) / kDecodeMinChunk;
+  if (parts > want) parts = want;
+  const size_t rows = (size_t)d->batch * d->q_heads * d->q_len;
+  DecodeLayout L;
+  L.o_off = 0;
+  L.m_off = align256((size_t)parts * rows * d->head_dim * sizeof(float));
+  L.l_off = L.m_off + align256((size_t)parts * rows * sizeof(float));
+  L.total = rows && parts ? L.l_off + align256((size_t)parts * rows * sizeof(float)) : 0;
+  return L;
+}
+
 }  // namespace
 
 extern "C" {
@@ -298,10 +353,10 @@ int ra_block_step(ra_state* st, const void* k, const void* v, int32_t kv_len, in
     p.l = st->l + b.row0;
     p.q_sb = d->q_strides[0];
     p.q_sh = d->q_strides[1];
-    p.q_st = d->q_strides[2];
+    p.q_st = token_stride(d->q_strides[2], d->q_len, d->head_dim);
     p.k_sb = d->kv_strides[0];
     p.k_sh = d->kv_strides[1];
-    p.k_st = d->kv_strides[2];
+    p.k_st = token_stride(d->kv_strides[2], kv_len, d->head_dim);
     p.batch = d->batch;
     p.q_heads = d->q_heads;
     p.kv_heads = d->kv_heads;
@@ -397,6 +452,92 @@ int ra_merge_states(const ra_desc* desc, int32_t n_parts, void* const* parts, vo
   p.d = desc->head_dim;
   hipError_t e = ra::launch_merge(p, static_cast<hipStream_t>(desc->stream));
   if (e != hipSuccess) return hip_fail(e, "merge kernel launch");
+  return RA_OK;
+}
+
+size_t ra_decode_workspace_bytes(const ra_desc* desc, int32_t kv_len) {
+  if (check_desc(desc) || kv_len < 0) return 0;
+  return decode_layout(desc, kv_len).total;
+}
+
+int ra_decode_step(ra_state* st, const void* k, const void* v, int32_t kv_len, int32_t mask_kind,
+                   int64_t q_offset, int64_t k_offset, void* workspace, size_t workspace_bytes) {
+  if (!st) return fail(RA_E_INVALID, "state is NULL");
+  if (st->finalized) return fail(RA_E_STATE, "step after finalize");
+  const ra_desc* d = &st->desc;
+  if (d->dtype != RA_DTYPE_BF16) return fail(RA_E_UNSUPPORTED, "the split-KV step runs on bf16 inputs");
+  if (mask_kind == RA_MASK_CAUSAL_ZIGZAG)
+    return fail(RA_E_UNSUPPORTED, "the split-KV step takes single-range layouts (not zigzag)");
+  ra_stats s;
+  Sub subs[4];
+  int n_subs = 0;
+  int rc = plan(d, kv_len, mask_kind, q_offset, k_offset, &s, subs, &n_subs);
+  if (rc) return rc;
+  if (kv_len > 0) {
+    if (!k || !v) return fail(RA_E_INVALID, "K_j or V_j is NULL");
+    if (!aligned16(k) || !aligned16(v)) return fail(RA_E_INVALID, "K_j and V_j must be 16-byte aligned");
+    if (kv_len > 1 && d->kv_strides[2] < d->head_dim)
+      return fail(RA_E_INVALID, "kv token stride smaller than head_dim");
+  }
+  if (s.blocks_run == 0) {
+    add_stats(&st->stats, &s);
+    return RA_OK;
+  }
+  const DecodeLayout L = decode_layout(d, kv_len);
+  if (!workspace) return fail(RA_E_INVALID, "workspace is NULL");
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255) != 0)
+    return fail(RA_E_INVALID, "workspace must be 256-byte aligned");
+  if (workspace_bytes < L.total)
+    return fail(RA_E_INVALID, "workspace holds %zu bytes, the block needs %zu", workspace_bytes, L.total);
+  // keys past the last row's causal limit are seen by no row
+  const Sub& b = subs[0];
+  const int32_t n_keys = ra::keys_visible(d->q_len - 1, b.diag, kv_len);
+  const DecodePlan pl = decode_plan(d, n_keys);
+  const int64_t grid = (int64_t)pl.n_parts * decode_row_groups(d) * d->kv_heads * d->batch;
+  if (grid * 64 > 0xffffffffLL)   // a launch holds fewer than 2^32 work-items
+    return fail(RA_E_UNSUPPORTED, "split-KV grid of %lld waves is too large", (long long)grid);
+  char* ws = static_cast<char*>(workspace);
+  ra::DecodeParams p;
+  p.q = st->q;
+  p.k = k;
+  p.v = v;
+  p.part_o = reinterpret_cast<float*>(ws + L.o_off);
+  p.part_m = reinterpret_cast<float*>(ws + L.m_off);
+  p.part_l = reinterpret_cast<float*>(ws + L.l_off);
+  p.q_sb = d->q_strides[0];
+  p.q_sh = d->q_strides[1];
+  p.q_st = token_stride(d->q_strides[2], d->q_len, d->head_dim);
+  p.k_sb = d->kv_strides[0];
+  p.k_sh = d->kv_strides[1];
+  p.k_st = token_stride(d->kv_strides[2], kv_len, d->head_dim);
+  p.batch = d->batch;
+  p.q_heads = d->q_heads;
+  p.kv_heads = d->kv_heads;
+  p.group = d->q_heads / d->kv_heads;
+  p.n_q = d->q_len;
+  p.n_k = n_keys;
+  p.n_parts = pl.n_parts;
+  p.chunk = pl.chunk;
+  p.diag = b.diag;
+  p.scale_log2 = d->softmax_scale * 1.4426950408889634f;
+  hipStream_t stream = static_cast<hipStream_t>(d->stream);
+  hipError_t e = ra::launch_decode(p, d->head_dim, stream);
+  if (e != hipSuccess) return hip_fail(e, "split-KV step launch");
+  ra::CombineParams c;
+  c.part_o = p.part_o;
+  c.part_m = p.part_m;
+  c.part_l = p.part_l;
+  c.n_parts = pl.n_parts;
+  c.o_acc = st->o_acc;
+  c.m = st->m;
+  c.l = st->l;
+  c.rows = (int64_t)d->batch * d->q_heads * d->q_len;
+  c.d = d->head_dim;
+  c.fresh = st->fresh;
+  e = ra::launch_combine(c, stream);
+  if (e != hipSuccess) return hip_fail(e, "split-KV combine launch");
+  st->fresh = 0;
+  add_stats(&st->stats, &s);
   return RA_OK;
 }
 
@@ -497,10 +638,10 @@ int ra_bwd_block_step(ra_bwd* st, const void* k, const void* v, float* dk, float
     p.dv = dv + (int64_t)b.key0 * d->head_dim;
     p.q_sb = d->q_strides[0];
     p.q_sh = d->q_strides[1];
-    p.q_st = d->q_strides[2];
+    p.q_st = token_stride(d->q_strides[2], d->q_len, d->head_dim);
     p.k_sb = d->kv_strides[0];
     p.k_sh = d->kv_strides[1];
-    p.k_st = d->kv_strides[2];
+    p.k_st = token_stride(d->kv_strides[2], kv_len, d->head_dim);
     p.batch = d->batch;
     p.q_heads = d->q_heads;
     p.kv_heads = d->kv_heads;

@@ -1,0 +1,354 @@
+// ra_decode.hip -- a KV block scored by a few query rows, split over the chip: the decode
+// path of "Ring Attention：把超长序列沿设备环流动", section 训练与推理的适用方式不同.  There the
+// query goes to every KV shard, each shard forms a local attention state and a global
+// online-softmax reduction combines the states.  The same two stages run here inside one
+// block: the keys are cut into chunks, one wave per chunk forms a local state, and
+// combine_kernel folds the chunk states (and the running state of the lap) into the state.
+// The shard states of different ranks are combined the same way by ra_merge.hip.
+//
+// A wave owns one (batch, KV head, group of 32 packed query rows, key chunk).  The packed rows
+// are the (query head of the group, query token) pairs that read this KV head, so a GQA group
+// of 8 heads decoding one token fills 8 of the matrix instruction's 32 columns, where the
+// 128-row step tile would hold one head's single row.  Per 32-key tile: S^T = K Q^T (K rows
+// straight from HBM into registers as operand A, q resident as operand B), the online-softmax
+// update in base 2 with an exact rescale, and O~^T += V^T P^T with V staged in LDS by
+// buffer_load ... lds and read back transposed by ds_read_b64_tr_b16.  The next tile's K and V
+// are in flight while the current one is computed.  A chunk with no key, or a row that sees
+// none of a chunk's keys, gives the empty state (m = -inf, l = 0, O~ = 0), which the
+// reduction weighs by zero.  Reading K and V once is the bound: HBM.
+
+#include <hip/hip_runtime.h>
+
+#include <type_traits>
+
+#include "ra_internal.h"
+#include "ra_pos.h"
+
+namespace ra {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __attribute__((address_space(3))) void lds_void;
+
+constexpr int BK = kDecodeTileK;   // keys per tile
+
+// s_waitcnt with vmcnt = N (six bits: [3:0] and [15:14]); expcnt and lgkmcnt not waited on
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt has six bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// V tile [BK][D] in LDS: a 16-lane group of ds_read_b64_tr_b16 fetches four consecutive keys
+// x four 8-byte column pieces; this chunk twist puts a 32-lane half on distinct banks
+template <int D>
+__device__ __forceinline__ int v_swz(int t, int c) {
+  if constexpr (D == 128) return c ^ (4 * (t & 3));
+  else return c ^ (4 * ((t >> 1) & 1));
+}
+
+__device__ __forceinline__ void load_lds_b128_dec(__amdgpu_buffer_rsrc_t r, void* lds, int voff, int soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 16, voff, soff, 0, 0);
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_dec(const void* base, int64_t bytes) {
+  const int n = bytes > 0x7fffffff ? 0x7fffffff : (int)(bytes < 0 ? 0 : bytes);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, 0x00020000);
+}
+
+__device__ __forceinline__ void pair32_dec(float x, float& a, float& b) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  a = __uint_as_float(r[0]);
+  b = __uint_as_float(r[1]);
+}
+
+template <int D>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void decode_kernel(DecodeParams p) {
+  constexpr int KS = D / 16, VB = D / 32, RB = D * 2, CPR = D / 8, RPL = 64 / CPR;
+  constexpr int LPT = BK * RB / 1024;   // 1 KB direct loads per V tile
+  __shared__ __attribute__((aligned(16))) unsigned char v_t0[BK * RB];
+  __shared__ __attribute__((aligned(16))) unsigned char v_t1[BK * RB];
+
+  const int lane = threadIdx.x;
+  const int r32 = lane & 31, hi = lane >> 5;
+  // grid: (part, row group, KV head, batch), part fastest
+  int L = blockIdx.x;
+  const int part = L % p.n_parts;
+  L /= p.n_parts;
+  const int n_rg = (p.group * p.n_q + 31) / 32;
+  const int rg = L % n_rg;
+  L /= n_rg;
+  const int g = L % p.kv_heads;
+  const int b = L / p.kv_heads;
+
+  // packed row -> (query head of the group, token)
+  const int pr = rg * 32 + r32;
+  const bool row_ok = pr < p.group * p.n_q;
+  const int hh = row_ok ? pr / p.n_q : 0;
+  const int i = row_ok ? pr - hh * p.n_q : 0;
+  const int h = g * p.group + hh;
+  const int64_t srow = ((int64_t)b * p.q_heads + h) * p.n_q + i;
+
+  // this part's keys
+  const int chunk = p.chunk;
+  const int k0 = part * chunk;
+  const int k1 = min(k0 + chunk, p.n_k);
+  const int n_tiles = k1 > k0 ? (k1 - k0 + BK - 1) / BK : 0;
+
+  bf16x8 qf[KS];
+  {
+    const __bf16* qp = static_cast<const __bf16*>(p.q) + (int64_t)b * p.q_sb + (int64_t)h * p.q_sh + (int64_t)i * p.q_st + hi * 8;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      if (row_ok) {
+        qf[ks] = *reinterpret_cast<const bf16x8*>(qp + ks * 16);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qf[ks][e] = (__bf16)0.0f;
+      }
+    }
+  }
+  const float c2 = p.scale_log2;
+  float m_run = -INFINITY, l_run = 0.f;
+  f32x16 oacc[VB];
+#pragma unroll
+  for (int vb = 0; vb < VB; ++vb)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) oacc[vb][j] = 0.f;
+
+  const __bf16* kg = static_cast<const __bf16*>(p.k) + (int64_t)b * p.k_sb + (int64_t)g * p.k_sh;
+  const __bf16* vg = static_cast<const __bf16*>(p.v) + (int64_t)b * p.k_sb + (int64_t)g * p.k_sh;
+  const int row_bytes = (int)(p.k_st * 2);
+  // K operand A straight from HBM: lane reads key r32 of the tile, chunk 2*ks + hi
+  auto load_k = [&](int t0, bf16x8 (&kr)[KS]) {
+    const __amdgpu_buffer_rsrc_t r = rsrc_dec(kg + (int64_t)t0 * p.k_st, ((int64_t)k1 - t0) * p.k_st * 2);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const auto x = __builtin_amdgcn_raw_buffer_load_b128(r, r32 * row_bytes + (2 * ks + hi) * 16, 0, 0);
+      __builtin_memcpy(&kr[ks], &x, sizeof x);
+    }
+  };
+  // V tile into LDS: lane writes row lane / CPR of each 1 KB span at physical chunk lane % CPR
+  auto load_v = [&](unsigned char* tile, int t0) {
+    const __amdgpu_buffer_rsrc_t r = rsrc_dec(vg + (int64_t)t0 * p.k_st, ((int64_t)k1 - t0) * p.k_st * 2);
+#pragma unroll
+    for (int u = 0; u < LPT; ++u) {
+      const int row = u * RPL + lane / CPR;
+      const int voff = (lane / CPR) * row_bytes + v_swz<D>(row, lane % CPR) * 16;
+      load_lds_b128_dec(r, tile + u * RPL * RB, voff, u * RPL * row_bytes);
+    }
+  };
+  int v_roff[VB];
+  {
+    const int gg = lane >> 4, a = lane & 3, e = (lane >> 2) & 3;
+    const int key = 4 * (gg >> 1) + e;
+#pragma unroll
+    for (int vb = 0; vb < VB; ++vb) {
+      const int dv = 32 * vb + 16 * (gg & 1) + 4 * a;
+      v_roff[vb] = key * RB + (v_swz<D>(key, dv >> 3) << 4) + ((dv & 7) << 1);
+    }
+  }
+
+  // One tile: the next tile's K (registers kn) and V (the other LDS buffer) are put in flight
+  // first, then this tile (K in kc, V in buffer BUF) is computed.  The two V buffers are
+  // distinct objects and BUF is a compile-time constant, so the compiler can tell the buffer
+  // being read from the one a direct load is filling.
+  auto tile = [&](auto bufc, int tt, bf16x8 (&kc)[KS], bf16x8 (&kn)[KS]) {
+    constexpr int BUF = decltype(bufc)::value;
+    const unsigned char* cur = BUF ? v_t1 : v_t0;
+    const int t0 = k0 + tt * BK;
+    load_k(t0 + BK, kn);   // past the chunk's end: zeros, never used
+    load_v(BUF ? v_t0 : v_t1, t0 + BK);
+    wait_vmcnt<KS + LPT>();   // only the next tile's loads are outstanding: this tile's landed
+    __builtin_amdgcn_wave_barrier();
+    f32x16 s;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) s[j] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kc[ks], qf[ks], s, 0, 0, 0);
+    // lane holds keys t0 + 8*(j/4) + 4*hi + (j%4) of packed row pr
+    const int lim = min(i + p.diag, k1 - 1) - t0 - 4 * hi;
+    float mx = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      s[j] = (8 * (j >> 2) + (j & 3) > lim) ? -INFINITY : s[j];
+      mx = fmaxf(mx, s[j]);
+    }
+    {
+      float a, bb;
+      pair32_dec(mx, a, bb);
+      mx = fmaxf(a, bb);
+    }
+    const float m_new = fmaxf(m_run, mx * c2);
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+    bf16x8 pk[2];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) pk[j >> 3][j & 7] = (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(s[j], c2, -m_use));
+    float rs = 0.f;
+    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      rs = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pk[kk], pk[kk], 0, 1), ones, rs, false);
+      rs = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pk[kk], pk[kk], 2, 3), ones, rs, false);
+      rs = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pk[kk], pk[kk], 4, 5), ones, rs, false);
+      rs = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pk[kk], pk[kk], 6, 7), ones, rs, false);
+    }
+    {
+      float a, bb;
+      pair32_dec(rs, a, bb);
+      rs = a + bb;
+    }
+    l_run = l_run * alpha + rs;
+    m_run = m_new;
+#pragma unroll
+    for (int vb = 0; vb < VB; ++vb)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) oacc[vb][j] *= alpha;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int vb = 0; vb < VB; ++vb) {
+        const unsigned char* base = cur + v_roff[vb] + kk * 16 * RB;
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base));
+        const s16x4 hi8 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + 8 * RB));
+        const s16x8 both = __builtin_shufflevector(lo, hi8, 0, 1, 2, 3, 4, 5, 6, 7);
+        bf16x8 a;
+        __builtin_memcpy(&a, &both, sizeof a);
+        oacc[vb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pk[kk], oacc[vb], 0, 0, 0);
+      }
+    // every lane is done reading this V tile before the next iteration's copy overwrites it
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0), vmcnt and expcnt not waited on
+    __builtin_amdgcn_wave_barrier();
+  };
+
+  bf16x8 ka[KS], kb[KS];
+  if (n_tiles > 0) {
+    load_k(k0, ka);
+    load_v(v_t0, k0);
+  }
+  for (int tt = 0; tt < n_tiles; tt += 2) {
+    tile(std::integral_constant<int, 0>{}, tt, ka, kb);
+    if (tt + 1 < n_tiles) tile(std::integral_constant<int, 1>{}, tt + 1, kb, ka);
+  }
+  wait_vmcnt<0>();   // the last prefetch (zeros past the chunk) is not left in flight
+
+  if (row_ok) {
+    const int64_t rows = (int64_t)p.batch * p.q_heads * p.n_q;
+    const int64_t prow = (int64_t)part * rows + srow;
+    if (hi == 0) {
+      p.part_m[prow] = m_run;
+      p.part_l[prow] = l_run;
+    }
+    float* op = p.part_o + prow * D + 4 * hi;
+#pragma unroll
+    for (int vb = 0; vb < VB; ++vb)
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+        *reinterpret_cast<float4*>(op + vb * 32 + 8 * a) =
+            make_float4(oacc[vb][4 * a + 0], oacc[vb][4 * a + 1], oacc[vb][4 * a + 2], oacc[vb][4 * a + 3]);
+  }
+}
+
+// One workgroup per state row: the maximum over the parts (and the state unless fresh), then
+// l = sum_s 2^(m_s - m) l_s and O~ = sum_s 2^(m_s - m) O~_s, each thread summing one float4
+// column over a strided subset of the parts, and the subsets added through LDS.
+template <int D>
+__global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
+  constexpr int C4 = D / 4;      // float4 columns of a row
+  constexpr int PL = 256 / C4;   // parts summed side by side
+  __shared__ float red[256];
+  __shared__ float4 acc_s[PL][C4];
+  __shared__ float l_s[PL];
+  const int tid = threadIdx.x;
+  const int c = tid % C4, pl = tid / C4;
+  for (int64_t row = blockIdx.x; row < p.rows; row += gridDim.x) {
+    float mx = -INFINITY;
+    for (int s = tid; s < p.n_parts; s += 256) mx = fmaxf(mx, p.part_m[(int64_t)s * p.rows + row]);
+    if (!p.fresh && tid == 0) mx = fmaxf(mx, p.m[row]);
+    red[tid] = mx;
+    __syncthreads();
+    for (int w = 128; w > 0; w >>= 1) {
+      if (tid < w) red[tid] = fmaxf(red[tid], red[tid + w]);
+      __syncthreads();
+    }
+    const float M = red[0];
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    float ls = 0.f;
+    auto add = [&](float ms, float l, const float* o) {
+      const float w = ms == -INFINITY ? 0.f : exp2f(ms - M);
+      const float4 x = *reinterpret_cast<const float4*>(o + 4 * c);
+      acc.x += w * x.x;
+      acc.y += w * x.y;
+      acc.z += w * x.z;
+      acc.w += w * x.w;
+      ls += w * l;
+    };
+    for (int s = pl; s < p.n_parts; s += PL) {
+      const int64_t pr = (int64_t)s * p.rows + row;
+      add(p.part_m[pr], p.part_l[pr], p.part_o + pr * D);
+    }
+    if (!p.fresh && pl == 0) add(p.m[row], p.l[row], p.o_acc + row * D);
+    acc_s[pl][c] = acc;
+    if (c == 0) l_s[pl] = ls;
+    __syncthreads();
+    if (pl == 0) {
+      for (int u = 1; u < PL; ++u) {
+        const float4 x = acc_s[u][c];
+        acc.x += x.x;
+        acc.y += x.y;
+        acc.z += x.z;
+        acc.w += x.w;
+      }
+      *reinterpret_cast<float4*>(p.o_acc + row * D + 4 * c) = acc;
+      if (c == 0) {
+        for (int u = 1; u < PL; ++u) ls += l_s[u];
+        p.m[row] = M;
+        p.l[row] = ls;
+      }
+    }
+    __syncthreads();   // red, acc_s and l_s are reused by the next row
+  }
+}
+
+}  // namespace
+
+hipError_t launch_combine(const CombineParams& p, hipStream_t stream) {
+  if (p.rows == 0) return hipSuccess;
+  const unsigned grid = (unsigned)(p.rows < 65536 ? p.rows : 65536);
+  switch (p.d) {
+    case 64:
+      hipLaunchKernelGGL(combine_kernel<64>, dim3(grid), dim3(256), 0, stream, p);
+      break;
+    case 128:
+      hipLaunchKernelGGL(combine_kernel<128>, dim3(grid), dim3(256), 0, stream, p);
+      break;
+    default:
+      return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_decode(const DecodeParams& p, int head_dim, hipStream_t stream) {
+  const int n_rg = (p.group * p.n_q + 31) / 32;
+  const int64_t grid = (int64_t)p.n_parts * n_rg * p.kv_heads * p.batch;
+  if (grid == 0) return hipSuccess;
+  switch (head_dim) {
+    case 64:
+      hipLaunchKernelGGL(decode_kernel<64>, dim3((unsigned)grid), dim3(64), 0, stream, p);
+      break;
+    case 128:
+      hipLaunchKernelGGL(decode_kernel<128>, dim3((unsigned)grid), dim3(64), 0, stream, p);
+      break;
+    default:
+      return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace ra

@@ -55,6 +55,39 @@ struct MergeParams {
   int32_t d;
 };
 
+// Split-KV step for a few query rows: the keys [0, n_k) of the block are cut into n_parts
+// chunks of `chunk` keys; chunk s's local state of every row goes to part_o / part_m /
+// part_l at [s, row], rows = B * Hq * n_q in the state's order.
+struct DecodeParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  float* part_o;       // [n_parts, rows, D]
+  float* part_m;       // [n_parts, rows], base 2
+  float* part_l;       // [n_parts, rows]
+  int64_t q_sb, q_sh, q_st;
+  int64_t k_sb, k_sh, k_st;
+  int32_t batch, q_heads, kv_heads, group;
+  int32_t n_q, n_k;
+  int32_t n_parts, chunk;
+  int32_t diag;
+  float scale_log2;
+};
+
+// Folds the parts of a split-KV step (and the state itself unless fresh) into the state.
+struct CombineParams {
+  const float* part_o;
+  const float* part_m;
+  const float* part_l;
+  int32_t n_parts;
+  float* o_acc;
+  float* m;
+  float* l;
+  int64_t rows;
+  int32_t d;
+  int32_t fresh;
+};
+
 // Backward: D = rowsum(dO * O) for every row of the state, and the dQ accumulator cleared.
 struct BwdPrepParams {
   const void* d_out;   // [B, Hq, n, d] in the input dtype, Q's strides
@@ -91,11 +124,15 @@ constexpr int kBf16TileQ = 128;
 constexpr int kBf16TileK = 64;
 constexpr int kF32TileQ = 64;
 constexpr int kF32TileK = 32;
+constexpr int kDecodeRows = 32;   // packed (query head, token) rows per wave of the split-KV step
+constexpr int kDecodeTileK = 32;
 
 hipError_t launch_step_bf16(const StepParams& p, int head_dim, hipStream_t stream);
 hipError_t launch_step_f32(const StepParams& p, int head_dim, hipStream_t stream);
 hipError_t launch_finalize(const FinalizeParams& p, hipStream_t stream);
 hipError_t launch_merge(const MergeParams& p, hipStream_t stream);
+hipError_t launch_decode(const DecodeParams& p, int head_dim, hipStream_t stream);
+hipError_t launch_combine(const CombineParams& p, hipStream_t stream);
 hipError_t launch_bwd_prep(const BwdPrepParams& p, int head_dim, bool bf16, hipStream_t stream);
 hipError_t launch_bwd_step_f32(const BwdParams& p, int head_dim, hipStream_t stream);
 hipError_t launch_bwd_step_bf16(const BwdParams& p, int head_dim, hipStream_t stream);

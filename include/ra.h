@@ -196,6 +196,29 @@ int ra_state_set_debug_counters(ra_state* st, uint64_t* counters);
 int ra_merge_states(const ra_desc* desc, int32_t n_parts, void* const* parts, void* merged,
                     float* o, float* lse);
 
+/* ---- the block step for a few query rows (split-KV) -------------------------------- */
+
+/* Bytes of device workspace that ra_decode_step needs for a block of kv_len keys under desc
+ * (0 if desc is invalid, q_len == 0 or kv_len == 0). */
+size_t ra_decode_workspace_bytes(const ra_desc* desc, int32_t kv_len);
+
+/* The same update of the state as ra_block_step (same arguments, same result up to the order
+ * of fp32 rounding, same stats and skip rule), computed the way "Ring Attention：把超长序列沿设备
+ * 环流动", section 训练与推理的适用方式不同, computes decode: the few query rows are sent to many
+ * shards of the keys, each shard forms a local state (m, l, O~), and a global online-softmax
+ * reduction combines the local states with the running state.  Here the shards are chunks of
+ * K_j/V_j, one wave of the chip each, so a block is streamed by the whole chip even when
+ * B * Hq * q_len is far below one 128-row tile; the query heads of a GQA group are packed into
+ * one wave.  Meant for short Q (decode, q_len up to a few tens); any q_len is accepted.
+ * workspace: device, 256-byte aligned, at least ra_decode_workspace_bytes(desc, kv_len)
+ * bytes (workspace_bytes says how many the caller passed); it holds the chunk states and is
+ * free again once the enqueued work has completed.  Errors: RA_E_UNSUPPORTED for fp32 inputs
+ * or RA_MASK_CAUSAL_ZIGZAG; RA_E_INVALID for a missing or short workspace and everything
+ * ra_block_step rejects. */
+int ra_decode_step(ra_state* st, const void* k, const void* v, int32_t kv_len,
+                   int32_t mask_kind, int64_t q_offset, int64_t k_offset, void* workspace,
+                   size_t workspace_bytes);
+
 /* ---- backward of the lap ------------------------------------------------------------ */
 
 /* The backward pass runs the same lap with gradients travelling too ("Ring Attention：把超长序

@@ -22,6 +22,13 @@ Recipe (one independent stream per (tensor, slab)):
 
 Because each slab has its own stream, any single head can be regenerated on
 its own (the sampled-row parity checks at full size rely on this).
+
+Device draws (``draw_device``): for inputs too large to draw on the host in a
+test's time (decode against a million keys), each slab is drawn on the GPU with
+torch's device generator seeded from the same SeedSequence words, as
+``randn((n, d), float32) * value_scale`` rounded to the dtype.  These are other
+numbers than the host draws of the same slab; the oracle side is then fed a
+host copy of the very tensors the device side reads.
 """
 
 from __future__ import annotations
@@ -112,6 +119,24 @@ def draw(seed: int, tensor_id: int, part: int, B: int, H: int, n: int, d: int,
     else:
         for j in jobs:
             one(j)
+    return out
+
+
+def draw_device(seed: int, tensor_id: int, part: int, B: int, H: int, n: int, d: int,
+                value_scale: float, dtype: str, device):
+    """[B, H, n, d] drawn on ``device`` in the workload dtype (see the module docstring)."""
+    import torch
+    tdt = {"bf16": torch.bfloat16, "f32": torch.float32}[dtype]
+    out = torch.empty((B, H, n, d), dtype=tdt, device=device)
+    for b in range(B):
+        for h in range(H):
+            word = np.random.SeedSequence([seed, tensor_id, part + 1, b, h]).generate_state(1, np.uint64)[0]
+            g = torch.Generator(device=device)
+            g.manual_seed(int(word) & ((1 << 63) - 1))
+            x = torch.randn((n, d), generator=g, device=device, dtype=torch.float32)
+            if value_scale != 1.0:
+                x.mul_(value_scale)
+            out[b, h].copy_(x)
     return out
 
 

@@ -323,3 +323,59 @@ def test_one_hip_runtime_per_process():
     the process would receive torch's stream handles and crash."""
     import torch  # noqa: F401
     assert len(_abi._hip_runtimes_mapped()) == 1
+
+
+def test_decode_workspace_bytes():
+    # chunk states: min(ceil(2048 waves / (B * Hkv * row groups of 32 packed rows)),
+    # ceil(kv_len / 256)) parts of rows * (d + 2) floats, each section 256-byte aligned
+    lib = ra.lib()
+    d = _desc(q_len=1, q_heads=64, kv_heads=8)            # 8 packed rows per KV head: one group
+    rows = 64
+
+    def expect(parts):
+        a = lambda x: (x + 255) // 256 * 256               # noqa: E731
+        return a(parts * rows * 128 * 4) + 2 * a(parts * rows * 4)
+
+    assert lib.ra_decode_workspace_bytes(C.byref(d), 1 << 20) == expect(256)
+    assert lib.ra_decode_workspace_bytes(C.byref(d), 300) == expect(2)
+    assert lib.ra_decode_workspace_bytes(C.byref(d), 1) == expect(1)
+    assert lib.ra_decode_workspace_bytes(C.byref(d), 0) == 0
+    assert lib.ra_decode_workspace_bytes(C.byref(d), -1) == 0
+    d2 = _desc(q_len=5, q_heads=16, kv_heads=2)           # 40 packed rows: two groups per KV head
+    a = lambda x: (x + 255) // 256 * 256                   # noqa: E731
+    parts = -(-2048 // (2 * 2))
+    assert lib.ra_decode_workspace_bytes(C.byref(d2), 1 << 20) == \
+        a(parts * 80 * 128 * 4) + 2 * a(parts * 80 * 4)
+    bad = _desc(q_len=1, d=96)
+    assert lib.ra_decode_workspace_bytes(C.byref(bad), 1000) == 0
+
+
+def test_decode_argument_validation():
+    # every check below is taken on the host before anything is enqueued
+    lib = ra.lib()
+    d = _desc(q_len=4, q_heads=8, kv_heads=2)
+    h = C.c_void_p()
+    assert lib.ra_state_init(C.byref(d), 0x10000, 0x20000, C.byref(h)) == ra.RA_OK
+    ws, K, V = 0x100000, 0x300000, 0x500000
+    need = lib.ra_decode_workspace_bytes(C.byref(d), 512)
+    E = ra.RA_E_INVALID
+    assert lib.ra_decode_step(None, K, V, 512, 0, 0, 0, ws, need) == E                      # no state
+    assert lib.ra_decode_step(h, K, V, 512, ra.RA_MASK_CAUSAL_ZIGZAG, 0, 0, ws, need) == ra.RA_E_UNSUPPORTED
+    assert lib.ra_decode_step(h, None, V, 512, 0, 0, 0, ws, need) == E                      # NULL K
+    assert lib.ra_decode_step(h, K + 4, V, 512, 0, 0, 0, ws, need) == E                     # misaligned
+    assert lib.ra_decode_step(h, K, V, 512, 0, 0, 0, None, need) == E                       # no workspace
+    assert lib.ra_decode_step(h, K, V, 512, 0, 0, 0, ws + 16, need) == E                    # misaligned
+    assert lib.ra_decode_step(h, K, V, 512, 0, 0, 0, ws, need - 1) == E                     # too short
+    assert lib.ra_decode_step(h, K, V, -1, 0, 0, 0, ws, need) == E                          # bad length
+    assert lib.ra_decode_step(h, K, V, 512, 9, 0, 0, ws, need) == E                         # bad mask
+    # blocks without an allowed pair launch nothing and need no workspace
+    assert lib.ra_decode_step(h, K, V, 512, ra.RA_MASK_CAUSAL_CONTIGUOUS, 0, 4, None, 0) == ra.RA_OK
+    assert lib.ra_decode_step(h, None, None, 0, 0, 0, 0, None, 0) == ra.RA_OK
+    s = ra.ra_stats()
+    assert lib.ra_get_stats(h, C.byref(s)) == ra.RA_OK
+    assert s.blocks_skipped == 2 and s.blocks_run == 0 and s.live_pairs == 0
+    lib.ra_state_destroy(h)
+    d32 = _desc(q_len=4, q_heads=8, kv_heads=2, dtype=ra.RA_DTYPE_F32)
+    assert lib.ra_state_init(C.byref(d32), 0x10000, 0x20000, C.byref(h)) == ra.RA_OK
+    assert lib.ra_decode_step(h, K, V, 512, 0, 0, 0, ws, need) == ra.RA_E_UNSUPPORTED
+    lib.ra_state_destroy(h)
