@@ -33,6 +33,7 @@ from .attention import (  # noqa: F401
     online_finalize,
     online_state_init,
     ring_visit_order,
+    shard_capacity,
     tile_classes,
     token_owner,
     tokens_of_rank,

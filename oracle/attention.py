@@ -28,6 +28,9 @@ state:
   [P2] body and [P3] Causal section; the map itself is this project's reading),
   or the paired "zigzag" layout: 2P chunks of N/(2P) tokens, rank r holding
   chunks r and 2P-1-r ([P1] "Striping the sequence to flatten the triangle").
+  When P does not divide N, contiguous shards are padded to ceil(N/P) slots and
+  the tail rank holds fewer real tokens ([P3] 正确性测试应覆盖哪些边界, tail-rank
+  padding with a valid-length mask): ``shard_capacity``.
 * The causal rule is on global positions: query q sees key k iff k <= q ([P3]
   Causal Attention 让环不再完全对称, and 位置编码必须使用全局位置).
 * ``merge_states`` is the global online-softmax reduction of shard states for
@@ -83,13 +86,23 @@ def ring_visit_order(P: int, r: int) -> list[int]:
     return seen
 
 
+def shard_capacity(N: int, P: int) -> int:
+    """Token slots per rank when N is split over P ranks: ceil(N / P).  When P does not
+    divide N, the shards are padded to this common size and the tail rank holds fewer real
+    tokens ([P3] 正确性测试应覆盖哪些边界: divisible and non-divisible N, tail-rank padding
+    with a valid-length mask)."""
+    return -(-N // P)
+
+
 def token_owner(N: int, P: int, layout: str) -> np.ndarray:
-    """Rank that owns each global token 0..N-1 under a layout."""
-    if N % P:
-        raise ValueError("N must be a multiple of P")
+    """Rank that owns each global token 0..N-1 under a layout.
+
+    Contiguous: rank r owns [r * c, min(N, (r + 1) * c)) with c = shard_capacity(N, P), so
+    for N not a multiple of P the last ranks own fewer tokens (possibly none).  Striped:
+    token t goes to rank t mod P for any N.  Zigzag needs N to be a multiple of 2P."""
     t = np.arange(N, dtype=np.int64)
     if layout == "contiguous":
-        return t // (N // P)
+        return t // shard_capacity(N, P)
     if layout == "striped":
         return t % P
     if layout == "zigzag":
@@ -163,7 +176,7 @@ def dense_attention(q, k, v, q_pos, k_pos, causal: bool, scale: float | None = N
                 s = scale * (q[b, h, ri] @ kh.T)                  # [rows, N]
                 ok = allowed_mask(q_pos[ri], k_pos, causal)
                 s = np.where(ok, s, -np.inf)
-                mx = s.max(axis=1, keepdims=True)
+                mx = s.max(axis=1, keepdims=True, initial=-np.inf)
                 has = np.isfinite(mx[:, 0])
                 mx_safe = np.where(np.isfinite(mx), mx, 0.0)
                 p = np.where(ok, np.exp(s - mx_safe), 0.0)
@@ -219,7 +232,7 @@ def online_block_update(state: dict, q, k_j, v_j, q_pos, k_pos_j, causal: bool,
         for h in range(Hq):
             s = scale * (q[b, h] @ k_j[b, h // G].T)                 # block scores S^(j)
             s = np.where(ok, s, -np.inf)
-            block_max = s.max(axis=1)                                # local max of this block
+            block_max = s.max(axis=1, initial=-np.inf)               # local max (-inf: no key)
             mn = np.maximum(m_old[b, h], block_max)                  # new running max
             # rows with no key seen so far: keep everything at the empty state
             live = np.isfinite(mn)

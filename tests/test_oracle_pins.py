@@ -107,6 +107,26 @@ def test_token_layouts():
         assert sorted(allpos.tolist()) == list(range(N))
 
 
+def test_token_layouts_when_P_does_not_divide_N():
+    # [P3] 正确性测试应覆盖哪些边界: N not a multiple of P, tail-rank padding.  Every shard has
+    # ceil(N/P) slots; contiguous device p local index i -> global p * ceil(N/P) + i for the
+    # slots that hold a real token; striped keeps token t on rank t mod P.
+    assert oracle.shard_capacity(23, 4) == 6 and oracle.shard_capacity(24, 4) == 6
+    assert oracle.shard_capacity(25, 4) == 7 and oracle.shard_capacity(1, 8) == 1
+    expect_contig = {0: [0, 1, 2, 3, 4, 5], 1: [6, 7, 8, 9, 10, 11], 2: [12, 13, 14, 15, 16, 17],
+                     3: [18, 19, 20, 21, 22]}
+    expect_striped = {0: [0, 4, 8, 12, 16, 20], 1: [1, 5, 9, 13, 17, 21], 2: [2, 6, 10, 14, 18, 22],
+                      3: [3, 7, 11, 15, 19]}
+    for p in range(4):
+        assert oracle.tokens_of_rank(23, 4, "contiguous", p).tolist() == expect_contig[p]
+        assert oracle.tokens_of_rank(23, 4, "striped", p).tolist() == expect_striped[p]
+    # N = 9 over 4 ranks: 3 slots each, the last rank holds no real token
+    assert [oracle.tokens_of_rank(9, 4, "contiguous", p).tolist() for p in range(4)] == \
+        [[0, 1, 2], [3, 4, 5], [6, 7, 8], []]
+    with pytest.raises(ValueError):
+        oracle.token_owner(23, 4, "zigzag")
+
+
 # ---------------------------------------------------------------------------
 # Dense attention against independent references
 # ---------------------------------------------------------------------------
@@ -195,16 +215,19 @@ def test_blockwise_equals_dense(layout, P, causal):
         assert np.max(np.abs(lse_ring[fin] - lse_ref[fin])) <= 1e-12
 
 
-@pytest.mark.parametrize("layout", ["contiguous", "striped", "zigzag"])
+@pytest.mark.parametrize("layout,N", [("contiguous", 64), ("striped", 64), ("zigzag", 64),
+                                      ("contiguous", 61), ("striped", 61), ("contiguous", 9)])
 @pytest.mark.parametrize("P", [2, 4])
-def test_whole_ring_equals_unsharded_causal_sdpa(layout, P):
+def test_whole_ring_equals_unsharded_causal_sdpa(layout, N, P):
     """Reassemble every rank's lap; it must equal causal attention on the full sequence.
 
     The reference here is torch's is_causal lower-triangular mask over global
-    token order: no position or layout code of the oracle is involved.
+    token order: no position or layout code of the oracle is involved.  N = 61 and 9 are
+    not multiples of P: padded shards whose tail rank holds fewer real tokens (for N = 9,
+    P = 4 the last rank holds none).
     """
-    rng = _rng(20 + P)
-    N, d, H = 64, 8, 2
+    rng = _rng(20 + P + N)
+    d, H = 8, 2
     q = rng.standard_normal((1, H, N, d))
     k = rng.standard_normal((1, H, N, d))
     v = rng.standard_normal((1, H, N, d))
