@@ -306,7 +306,9 @@ def block_offsets(mask_kind: int, rank: int, block: int, q_len: int, kv_len: int
 class EmulatedRing:
     """Buffers and streams for ra_ring_lap_emulated: two receive buffers and a side stream."""
 
-    def __init__(self, k_blocks, v_blocks, side_stream=None):
+    def __init__(self, k_blocks, v_blocks, side_stream=None, valid=None):
+        """``valid``: optional per-block counts of real keys (the rest of each block is padding;
+        see ra_lap.kv_valid)."""
         import torch
         if len(k_blocks) != len(v_blocks) or not k_blocks:
             raise ValueError("need one K and one V tensor per block")
@@ -323,6 +325,11 @@ class EmulatedRing:
         self._kp = (C.c_void_p * P)(*[t.data_ptr() for t in self.k_blocks])
         self._vp = (C.c_void_p * P)(*[t.data_ptr() for t in self.v_blocks])
         self.block_bytes = ref.numel() * ref.element_size()
+        self._valid = None
+        if valid is not None:
+            if len(valid) != P:
+                raise ValueError("need one valid count per block")
+            self._valid = (C.c_int32 * P)(*[int(x) for x in valid])
 
     def lap(self, q, rank: int, mask_kind: int, softmax_scale: float = 0.0, workspace=None,
             out=None, lse=None, poison: bool = False, stream=None, step_events=None):
@@ -356,6 +363,8 @@ class EmulatedRing:
                 raise ValueError("need 2P events")
             evs = (C.c_void_p * (2 * P))(*[int(e.cuda_event) for e in step_events])
             lap.step_events = C.cast(evs, C.POINTER(C.c_void_p))
+        if self._valid is not None:
+            lap.kv_valid = C.cast(self._valid, C.POINTER(C.c_int32))
         st = ra_stats()
         check(lib().ra_ring_lap_emulated(C.byref(desc), q.data_ptr(), workspace.data_ptr(),
                                          C.byref(lap), out.data_ptr(), lse.data_ptr(), C.byref(st)))

@@ -78,6 +78,7 @@ class ra_lap(C.Structure):
         ("poison", C.c_int32),
         ("side_stream", C.c_void_p),
         ("step_events", C.POINTER(C.c_void_p)),
+        ("kv_valid", C.POINTER(C.c_int32)),
     ]
 
 

@@ -15,6 +15,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include <cstdio>
+
 #include "../../include/ra.h"
 #include "ra_internal.h"
 
@@ -59,9 +61,15 @@ extern "C" int ra_ring_lap_emulated(const ra_desc* desc, const void* q, void* wo
         return ra::set_error(RA_E_INVALID, "receive buffers are NULL");
     if (lap->block_bytes == 0) return ra::set_error(RA_E_INVALID, "block_bytes is 0");
   }
-  for (int j = 0; j < P; ++j)
+  for (int j = 0; j < P; ++j) {
     if (lap->kv_len > 0 && (!lap->k_blocks[j] || !lap->v_blocks[j]))
       return ra::set_error(RA_E_INVALID, "a KV block pointer is NULL");
+    if (lap->kv_valid && (lap->kv_valid[j] < 0 || lap->kv_valid[j] > lap->kv_len)) {
+      char msg[96];
+      snprintf(msg, sizeof msg, "kv_valid[%d] = %d is outside [0, kv_len]", j, (int)lap->kv_valid[j]);
+      return ra::set_error(RA_E_INVALID, msg);
+    }
+  }
 
   StateGuard g;
   int rc = ra_state_init(desc, q, workspace, &g.st);
@@ -120,7 +128,9 @@ extern "C" int ra_ring_lap_emulated(const ra_desc* desc, const void* q, void* wo
     if (lap->step_events &&
         (e = hipEventRecord(static_cast<hipEvent_t>(lap->step_events[2 * s]), cs)) != hipSuccess)
       return ra::set_hip_error(e, "event record");
-    rc = ra_block_step(g.st, kp, vp, lap->kv_len, lap->mask_kind, q_off, k_off);
+    // padding past a block's real keys is cut off by the key count: no query sees it
+    const int32_t keys = lap->kv_valid ? lap->kv_valid[j] : lap->kv_len;
+    rc = ra_block_step(g.st, kp, vp, keys, lap->mask_kind, q_off, k_off);
     if (rc) return rc;
     if (lap->step_events &&
         (e = hipEventRecord(static_cast<hipEvent_t>(lap->step_events[2 * s + 1]), cs)) != hipSuccess)

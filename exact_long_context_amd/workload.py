@@ -38,6 +38,31 @@ def shard_blocks(k_global, v_global, P: int, layout: str):
     return ks, vs
 
 
+def shard_blocks_padded(k_global, v_global, P: int, layout: str, fill: float = float("nan")):
+    """Blocks of ceil(N/P) slots for any N (contiguous or striped): block j holds its real
+    tokens first and ``fill`` in the slots past them.  Returns (k_blocks, v_blocks, valid)
+    with valid[j] the count of real tokens of block j."""
+    import torch
+    B, H, N, d = k_global.shape
+    c = -(-N // P)
+    ks, vs, valid = [], [], []
+    for j in range(P):
+        if layout == "contiguous":
+            idx = torch.arange(j * c, min(N, (j + 1) * c), device=k_global.device)
+        elif layout == "striped":
+            idx = torch.arange(j, N, P, device=k_global.device)
+        else:
+            raise ValueError(f"padded shards for {layout!r} are not defined")
+        kb = torch.full((B, H, c, d), fill, dtype=k_global.dtype, device=k_global.device)
+        vb = torch.full((B, H, c, d), fill, dtype=v_global.dtype, device=v_global.device)
+        kb[:, :, :idx.numel()] = k_global[:, :, idx]
+        vb[:, :, :idx.numel()] = v_global[:, :, idx]
+        ks.append(kb)
+        vs.append(vb)
+        valid.append(int(idx.numel()))
+    return ks, vs, valid
+
+
 def useful_flops(live_pairs: int, head_dim: int) -> int:
     """4*d flops per allowed (query, key) pair per query head: 2d for the score, 2d for PV."""
     return 4 * head_dim * live_pairs

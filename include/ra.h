@@ -303,6 +303,17 @@ typedef struct ra_lap {
   void* const* step_events;     /* NULL, or host array [2P] of hipEvent_t created by the caller:
                                    [2s] is recorded on desc.stream just before step s's kernel
                                    (after its wait for the block) and [2s+1] just after it */
+  const int32_t* kv_valid;      /* NULL, or host array [P]: block j's first kv_valid[j] keys
+                                   (0 <= kv_valid[j] <= kv_len) are real tokens and the rest of
+                                   its kv_len slots are padding that no query sees: the shards
+                                   of an N that P does not divide, each padded to kv_len =
+                                   ceil(N/P) slots ("Ring Attention：把超长序列沿设备环流动", section
+                                   正确性测试应覆盖哪些边界: tail-rank padding with a valid-length
+                                   mask).  Positions keep the padded slots (contiguous: block j
+                                   starts at j * kv_len), so Q_r is passed padded to the same
+                                   q_len on every rank and the rows past a rank's real tokens
+                                   are padding whose outputs mean nothing.  The whole block
+                                   (block_bytes) still travels. */
 } ra_lap;
 
 int ra_ring_lap_emulated(const ra_desc* desc, const void* q, void* workspace,

@@ -316,6 +316,22 @@ def test_lap_argument_validation():
     assert lib.ra_ring_lap_emulated(C.byref(d), 0x10000, 0x20000, C.byref(lap), 0x50000, None,
                                     None) == ra.RA_E_INVALID
     assert lib.ra_ring_lap_emulated(None, 0, 0, None, 0, None, None) == ra.RA_E_INVALID
+    # per-block valid key counts must lie in [0, kv_len]; checked before any work is enqueued
+    kp = (C.c_void_p * 4)(0x100000, 0x200000, 0x300000, 0x400000)
+    lap = ra.ra_lap()
+    lap.k_blocks = C.cast(kp, C.POINTER(C.c_void_p))
+    lap.v_blocks = C.cast(kp, C.POINTER(C.c_void_p))
+    for i in range(2):
+        lap.recv_k[i] = 0x500000 + i * 0x100000
+        lap.recv_v[i] = 0x700000 + i * 0x100000
+    lap.block_bytes = 64 * 128 * 2
+    lap.rank = 1
+    lap.kv_len = 64
+    for bad in ([64, 64, 65, 3], [64, -1, 64, 64]):
+        valid = (C.c_int32 * 4)(*bad)
+        lap.kv_valid = C.cast(valid, C.POINTER(C.c_int32))
+        assert lib.ra_ring_lap_emulated(C.byref(d), 0x10000, 0x20000, C.byref(lap), 0x50000, None,
+                                        None) == ra.RA_E_INVALID
 
 
 def test_one_hip_runtime_per_process():

@@ -1,0 +1,107 @@
+"""GPU parity when P does not divide N: shards padded to ceil(N/P) slots with per-block valid
+key counts (tail-rank padding with a valid-length mask), through the emulated lap and through
+ra_block_step with ragged blocks, against the fp64 oracle over the real tokens only.  The
+padding is filled with NaN, so a padded key that reached a score or a value would show."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from gpu_util import assert_bf16_close, assert_f32_close, require_gpu, say, to64
+
+pytestmark = pytest.mark.gpu
+
+NONE, CONTIG, STRIPED = 0, 1, 2
+LAYOUT = {NONE: "contiguous", CONTIG: "contiguous", STRIPED: "striped"}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    require_gpu()
+    yield
+    torch.cuda.synchronize()
+
+
+def _padded_q(q_global, P, layout, r):
+    """Rank r's query rows padded to ceil(N/P) slots (zeros past its real tokens)."""
+    N = q_global.shape[2]
+    c = oracle.shard_capacity(N, P)
+    pos = oracle.tokens_of_rank(N, P, layout, r)
+    q = torch.zeros(q_global.shape[:2] + (c, q_global.shape[3]), dtype=q_global.dtype)
+    q[:, :, :pos.size] = q_global[:, :, torch.from_numpy(pos)]
+    return q, pos
+
+
+def _check(got, q_global, k, v, pos, causal, dtype, what):
+    N = k.shape[2]
+    if pos.size == 0:
+        return
+    ref, ref_lse = oracle.dense_attention(to64(q_global[:, :, torch.from_numpy(pos)]), to64(k), to64(v),
+                                          pos, np.arange(N), causal)
+    g = to64(got[0])[:, :, :pos.size]
+    if dtype == "bf16":
+        assert_bf16_close(g, ref, what)
+    else:
+        assert_f32_close(g, ref, what)
+    lse = to64(got[1])[:, :, :pos.size]
+    tol = 2e-2 if dtype == "bf16" else 1e-5
+    assert np.max(np.abs(lse - ref_lse)) <= tol * max(1.0, float(np.max(np.abs(ref_lse))))
+
+
+# (dtype, Hq, Hkv, d, N, P, mask)
+CASES = [
+    ("bf16", 4, 2, 128, 1001, 4, CONTIG),     # capacity 251: ranks 251, 251, 251, 248
+    ("bf16", 4, 2, 128, 1001, 4, STRIPED),    # ranks 251, 250, 250, 250
+    ("bf16", 2, 2, 64, 1001, 4, NONE),
+    ("f32", 2, 1, 128, 777, 8, CONTIG),       # capacity 98, last rank 91
+    ("f32", 2, 1, 64, 777, 8, STRIPED),
+    ("bf16", 2, 1, 128, 49, 8, CONTIG),       # capacity 7: the last rank holds no token
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: f"{c[0]}-N{c[4]}-P{c[5]}-m{c[6]}")
+def test_padded_emulated_lap_matches_oracle(case):
+    import exact_long_context_amd as ra
+    from exact_long_context_amd.workload import shard_blocks_padded
+    dtype, Hq, Hkv, d, N, P, mask = case
+    layout = LAYOUT[mask]
+    q_all, k, v = synth.random_case(1300 + N + mask, 1, Hq, Hkv, N, N, d, dtype)
+    kb, vb, valid = shard_blocks_padded(k.cuda(), v.cuda(), P, layout)
+    assert valid == [oracle.tokens_of_rank(N, P, layout, j).size for j in range(P)]
+    ring = ra.EmulatedRing(kb, vb, valid=valid)
+    for r in sorted({0, P // 2, P - 1}):
+        q, pos = _padded_q(q_all, P, layout, r)
+        say(f"  padded lap {case} rank {r}: {pos.size} real rows of {q.shape[2]}")
+        o, lse, stats = ring.lap(q.cuda(), r, mask, poison=True)
+        torch.cuda.synchronize()
+        _check((o, lse), q_all, k, v, pos, mask != NONE, dtype, f"rank {r} O")
+        # pairs counted by the planner are exactly the oracle's over real tokens (padding rows
+        # count as queries too: they sit at positions past N and see every real key before them)
+        kpos = [oracle.tokens_of_rank(N, P, layout, j) for j in range(P)]
+        c = q.shape[2]
+        qpos = (r * c + np.arange(c)) if layout == "contiguous" else (r + P * np.arange(c))
+        want = sum(oracle.live_pair_count(qpos, kp, mask != NONE) for kp in kpos) * Hq
+        assert stats["live_pairs"] == want
+
+
+def test_ragged_blocks_through_block_step():
+    """Blocks of different real lengths passed straight to ra_block_step (no padding at all):
+    the last block of a contiguous N = 1001, P = 4 split holds 248 keys."""
+    import exact_long_context_amd as ra
+    N, P, Hq, Hkv, d = 1001, 4, 4, 2, 128
+    q_all, k, v = synth.random_case(1400, 1, Hq, Hkv, N, N, d, "bf16")
+    c = oracle.shard_capacity(N, P)
+    kd, vd = k.cuda(), v.cuda()
+    r = 3
+    q, pos = _padded_q(q_all, P, "contiguous", r)
+    q = q[:, :, :pos.size].contiguous().cuda()      # only the real rows this time
+    st = ra.RingState(q, kd[:, :, :c], ring_size=P)
+    for j in oracle.ring_visit_order(P, r):
+        a, b = j * c, min(N, (j + 1) * c)
+        st.step(kd[:, :, a:b], vd[:, :, a:b], CONTIG, r * c, a)
+    o, lse = st.finalize()
+    torch.cuda.synchronize()
+    st.close()
+    _check((o, lse), q_all, k, v, pos, True, "bf16", "ragged-block lap O")
