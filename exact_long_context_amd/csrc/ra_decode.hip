@@ -280,20 +280,35 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
     const float M = red[0];
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
     float ls = 0.f;
-    auto add = [&](float ms, float l, const float* o) {
+    auto add = [&](float ms, float l, float4 x) {
       const float w = ms == -INFINITY ? 0.f : exp2f(ms - M);
-      const float4 x = *reinterpret_cast<const float4*>(o + 4 * c);
       acc.x += w * x.x;
       acc.y += w * x.y;
       acc.z += w * x.z;
       acc.w += w * x.w;
       ls += w * l;
     };
-    for (int s = pl; s < p.n_parts; s += PL) {
-      const int64_t pr = (int64_t)s * p.rows + row;
-      add(p.part_m[pr], p.part_l[pr], p.part_o + pr * D);
+    // U parts per pass, all loads issued before any is used
+    constexpr int U = 8;
+    int s = pl;
+    for (; s + (U - 1) * PL < p.n_parts; s += U * PL) {
+      float ms[U], lv[U];
+      float4 x[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int64_t pr = (int64_t)(s + u * PL) * p.rows + row;
+        ms[u] = p.part_m[pr];
+        lv[u] = p.part_l[pr];
+        x[u] = *reinterpret_cast<const float4*>(p.part_o + pr * D + 4 * c);
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) add(ms[u], lv[u], x[u]);
     }
-    if (!p.fresh && pl == 0) add(p.m[row], p.l[row], p.o_acc + row * D);
+    for (; s < p.n_parts; s += PL) {
+      const int64_t pr = (int64_t)s * p.rows + row;
+      add(p.part_m[pr], p.part_l[pr], *reinterpret_cast<const float4*>(p.part_o + pr * D + 4 * c));
+    }
+    if (!p.fresh && pl == 0) add(p.m[row], p.l[row], *reinterpret_cast<const float4*>(p.o_acc + row * D + 4 * c));
     acc_s[pl][c] = acc;
     if (c == 0) l_s[pl] = ls;
     __syncthreads();
