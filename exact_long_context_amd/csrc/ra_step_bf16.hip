@@ -29,8 +29,10 @@
 //    between lanes.
 //  * LDS rows are XOR-swizzled in 16-byte chunks for gfx950's 64 banks, so that both the
 //    direct copies and the operand reads hit distinct banks.
-//  * The running maximum may lag the true one by up to 2^8 in the terms; O~ and l are
-//    rescaled only when some row's maximum grew by more than that.
+//  * The reference m of a row may lag its true maximum: a tile's terms 2^(x - m) are taken
+//    as they come while their row sum stays <= 2^32.  The row maximum is computed, and O~
+//    and l rescaled, only for a row past that bound or one setting its first reference,
+//    which in practice is the first visible tile of each row.
 //  * Causal skipping: the workgroup visits only the key tiles that hold an allowed pair
 //    and applies the element mask only on tiles that cross the diagonal or pass the
 //    block's end (ra_pos.h).
@@ -107,9 +109,11 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, in
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, 0x00020000);
 }
 
-// The running maximum may lag the true one by up to this much (base 2) before O~ and l are
-// rescaled: every term 2^(x - m) then stays <= 2^8, and most tiles skip the rescale.
-constexpr float kLagMax = 8.0f;
+// The reference m of a row may lag its true maximum: a tile's terms 2^(x - m) are used as
+// they come as long as their row sum stays <= 2^32 (so every term does), which fp32 and bf16
+// hold without loss; only a row past that, or one setting its first reference, takes the
+// tile's maximum.  Most tiles compute no maximum at all.
+constexpr float kSumMax = 4294967296.0f;   // 2^32
 
 
 template <int D, bool DEBUG>
@@ -220,9 +224,9 @@ void step_bf16_kernel(StepParams p) {
   }
 
   f32x16 oacc[VB];
-  float m_run, l_run;
+  float m_run, l_run;   // m_run: the finite reference of l and O~ (0 before any key)
   if (p.fresh || !row_ok) {
-    m_run = -INFINITY;
+    m_run = 0.f;
     l_run = 0.f;
 #pragma unroll
     for (int vb = 0; vb < VB; ++vb)
@@ -231,6 +235,7 @@ void step_bf16_kernel(StepParams p) {
   } else {
     m_run = p.m[srow];
     l_run = p.l[srow];
+    if (m_run == -INFINITY) m_run = 0.f;
     const float* op = p.o_acc + srow * D + 4 * hi;
 #pragma unroll
     for (int vb = 0; vb < VB; ++vb)
@@ -270,15 +275,11 @@ void step_bf16_kernel(StepParams p) {
   auto scores = [&](auto bufc, f32x16 (&sacc)[2]) {
     const unsigned char* kt_base = ktile(bufc);
 #pragma unroll
-    for (int kh = 0; kh < 2; ++kh)
-#pragma unroll
-      for (int j = 0; j < 16; ++j) sacc[kh][j] = 0.f;
-#pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
       for (int kh = 0; kh < 2; ++kh) {
         const bf16x8 a = *reinterpret_cast<const bf16x8*>(kt_base + k_roff[ks] + kh * 32 * RB);
-        sacc[kh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], sacc[kh], 0, 0, 0);
+        sacc[kh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], ks == 0 ? f32x16{} : sacc[kh], 0, 0, 0);
       }
     }
   };
@@ -306,63 +307,62 @@ void step_bf16_kernel(StepParams p) {
         for (int j = 0; j < 16; ++j) my_pairs += (sacc[kh][j] != -INFINITY) ? 1 : 0;
     }
 
-    // row max over the 64 keys: 32 in-lane values, then the partner lane
-    float mx = sacc[0][0];
+    // the next tile's scores: independent of everything below, so the matrix cores work
+    // on them while the vector unit forms this tile's probabilities
+    scores(knext, snext);
+
+    // probabilities 2^(x - m_run), rounded to bf16: the B operand of the value product; the
+    // row sum adds the same rounded values (v_dot2 with ones), so the weights used for O~ and
+    // for l agree exactly and a row with a single visible key normalises to exactly 1.  The
+    // sum also guards the reference: a row whose sum exceeds kSumMax grew too far above
+    // m_run, and a row that has seen nothing (l = 0) but has a visible key here must set its
+    // reference first.  Only then is the tile's maximum taken.
+    bf16x8 pk[4];
+    auto probs = [&](float shift) {
 #pragma unroll
-    for (int kh = 0; kh < 2; ++kh)
+      for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
-      for (int j = 0; j < 16; ++j) mx = fmaxf(mx, sacc[kh][j]);
-    {
+        for (int j = 0; j < 16; ++j)
+          pk[2 * kh + (j >> 3)][j & 7] = (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kh][j], c2, -shift));
+      float r = 0.f;
+      const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        r = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pk[kk], pk[kk], 0, 1), ones, r, false);
+        r = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pk[kk], pk[kk], 2, 3), ones, r, false);
+        r = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pk[kk], pk[kk], 4, 5), ones, r, false);
+        r = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pk[kk], pk[kk], 6, 7), ones, r, false);
+      }
       float a, bb;
-      pair32(mx, a, bb);
-      mx = fmaxf(a, bb);
-    }
-    // move the reference maximum only when some row of the wave grew by more than kLagMax
-    const float m_tile = mx * c2;
-    const bool grow = m_tile > m_run + kLagMax;
-    if (__builtin_amdgcn_ballot_w64(grow)) {
-      // rows that do not grow keep their reference (alpha = 1; this also keeps a row that
-      // has seen no key yet at -inf without forming -inf - -inf); a growing row from
-      // -inf gets alpha = 0 on its empty accumulators
-      const float alpha = grow ? __builtin_amdgcn_exp2f(m_run - m_tile) : 1.0f;
+      pair32(r, a, bb);
+      return a + bb;
+    };
+    float rs = probs(m_run);
+    const bool visible = kt * BK <= qrow + p.diag;
+    const bool bad = !(rs <= kSumMax) || (l_run == 0.f && visible);
+    if (__builtin_amdgcn_ballot_w64(bad)) {
+      float mx = sacc[0][0];
+#pragma unroll
+      for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) mx = fmaxf(mx, sacc[kh][j]);
+      {
+        float a, bb;
+        pair32(mx, a, bb);
+        mx = fmaxf(a, bb);
+      }
+      // a bad row moves its reference to the tile's maximum: l and O~ scale by 2^-shift
+      // (a row that has seen nothing holds zeros and takes 0: 2^-shift may overflow there)
+      // and this tile's probabilities are formed again
+      const float shift = (bad && mx != -INFINITY) ? mx * c2 - m_run : 0.f;
+      const float alpha = l_run == 0.f ? 0.f : __builtin_amdgcn_exp2f(-shift);
       l_run *= alpha;
 #pragma unroll
       for (int vb2 = 0; vb2 < VB; ++vb2)
 #pragma unroll
         for (int j = 0; j < 16; ++j) oacc[vb2][j] *= alpha;
-      m_run = grow ? m_tile : m_run;
-    }
-    const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
-
-    // the next tile's scores: independent of everything below, so the matrix cores work
-    // on them while the vector unit forms this tile's probabilities
-    scores(knext, snext);
-
-    // probabilities, rounded to bf16: the B operand of the value product; the row sum
-    // adds the same rounded values (v_dot2 with ones), so the weights used for O~ and for
-    // l agree exactly and a row with a single visible key normalises to exactly 1
-    bf16x8 pk[4];
-#pragma unroll
-    for (int kh = 0; kh < 2; ++kh)
-#pragma unroll
-      for (int j = 0; j < 16; ++j)
-        pk[2 * kh + (j >> 3)][j & 7] =
-            (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kh][j], c2, -m_use));
-    float rs = 0.f;
-    {
-      const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        rs = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pk[kk], pk[kk], 0, 1), ones, rs, false);
-        rs = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pk[kk], pk[kk], 2, 3), ones, rs, false);
-        rs = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pk[kk], pk[kk], 4, 5), ones, rs, false);
-        rs = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pk[kk], pk[kk], 6, 7), ones, rs, false);
-      }
-    }
-    {
-      float a, bb;
-      pair32(rs, a, bb);
-      rs = a + bb;
+      m_run += shift;
+      rs = probs(m_run);
     }
     l_run += rs;
 
@@ -412,7 +412,7 @@ void step_bf16_kernel(StepParams p) {
   // ---- write the state back ----------------------------------------------------------
   if (row_ok) {
     if (hi == 0) {
-      p.m[srow] = m_run;
+      p.m[srow] = l_run == 0.f ? -INFINITY : m_run;
       p.l[srow] = l_run;
     }
     float* op = p.o_acc + srow * D + 4 * hi;

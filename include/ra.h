@@ -123,10 +123,10 @@ typedef struct ra_state ra_state; /* opaque, host-side, owned by the library */
 /* Bytes of device workspace that holds the state (O~, m, l) for desc; 0 if desc is
  * invalid or q_len == 0.  Layout (all fp32, 256-byte aligned sections):
  *   O~ [B, Hq, n, d] at offset 0, m [B, Hq, n], l [B, Hq, n] at the offsets that
- *   ra_workspace_layout reports.  m is kept in base-2 units: it is the reference
- *   maximum of log2(e) * scale * <q, k> over the keys seen, and
- *   l = sum 2^(log2(e)*scale*<q,k> - m), O~ = sum 2^(...) v.  A valid state satisfies
- *   m >= max seen - 8, so every term stays <= 2^8. */
+ *   ra_workspace_layout reports.  m is kept in base-2 units: with x = log2(e) * scale *
+ *   <q, k> over the keys seen, m is a reference point and l = sum 2^(x - m),
+ *   O~ = sum 2^(x - m) v.  The kernels keep max x - 32 <= m <= max x, so every term stays
+ *   <= 2^32; a row that has seen no key holds m = -inf, l = 0, O~ = 0. */
 size_t ra_workspace_bytes(const ra_desc* desc);
 
 /* Byte offsets of O~, m and l inside the workspace (host out-pointers, any may be NULL). */
