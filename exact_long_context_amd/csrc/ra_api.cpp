@@ -521,7 +521,10 @@ int ra_decode_step(ra_state* st, const void* k, const void* v, int32_t kv_len, i
   p.diag = b.diag;
   p.scale_log2 = d->softmax_scale * 1.4426950408889634f;
   hipStream_t stream = static_cast<hipStream_t>(d->stream);
-  hipError_t e = ra::launch_decode(p, d->head_dim, stream);
+  // the row groups of one KV head share each chunk's tiles inside one workgroup
+  const int64_t n_rg = decode_row_groups(d);
+  const int waves = n_rg >= 3 ? 4 : (int)n_rg;
+  hipError_t e = ra::launch_decode(p, d->head_dim, waves, stream);
   if (e != hipSuccess) return hip_fail(e, "split-KV step launch");
   ra::CombineParams c;
   c.part_o = p.part_o;

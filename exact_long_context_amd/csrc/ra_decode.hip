@@ -67,22 +67,33 @@ __device__ __forceinline__ void pair32_dec(float x, float& a, float& b) {
   b = __uint_as_float(r[1]);
 }
 
-template <int D>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void decode_kernel(DecodeParams p) {
+// W waves per workgroup: the W row groups of one (part, KV head) share the chunk's V tiles in
+// LDS, each wave loading 1/W of every tile; their K loads are the same addresses at nearly the
+// same time, served once from HBM.  With one wave, two V buffers and no barrier; with several,
+// three buffers and one barrier per tile: a wave refills the buffer read two tiles earlier,
+// which every wave has finished by the time any wave passes the barrier of the tile between.
+template <int D, int W>
+__global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) void decode_kernel(DecodeParams p) {
   constexpr int KS = D / 16, VB = D / 32, RB = D * 2, CPR = D / 8, RPL = 64 / CPR;
   constexpr int LPT = BK * RB / 1024;   // 1 KB direct loads per V tile
+  static_assert(LPT % W == 0, "every wave loads the same share of a V tile");
+  constexpr int LPW = LPT / W;          // this wave's share
+  constexpr int NB = W == 1 ? 2 : 3;    // V buffers
   __shared__ __attribute__((aligned(16))) unsigned char v_t0[BK * RB];
   __shared__ __attribute__((aligned(16))) unsigned char v_t1[BK * RB];
+  __shared__ __attribute__((aligned(16))) unsigned char v_t2[NB == 3 ? BK * RB : 16];
 
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r32 = lane & 31, hi = lane >> 5;
-  // grid: (part, row group, KV head, batch), part fastest
+  // grid: (part, group of W row groups, KV head, batch), part fastest
   int L = blockIdx.x;
   const int part = L % p.n_parts;
   L /= p.n_parts;
   const int n_rg = (p.group * p.n_q + 31) / 32;
-  const int rg = L % n_rg;
-  L /= n_rg;
+  const int n_wg = (n_rg + W - 1) / W;
+  const int rg = (L % n_wg) * W + wave;   // past the last row group: a wave with no rows
+  L /= n_wg;
   const int g = L % p.kv_heads;
   const int b = L / p.kv_heads;
 
@@ -133,15 +144,21 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
       __builtin_memcpy(&kr[ks], &x, sizeof x);
     }
   };
-  // V tile into LDS: lane writes row lane / CPR of each 1 KB span at physical chunk lane % CPR
+  // this wave's share of a V tile into LDS: 1 KB span w*LPW + u holds key rows
+  // (w*LPW + u)*RPL + lane / CPR, lane at physical chunk lane % CPR
   auto load_v = [&](unsigned char* tile, int t0) {
     const __amdgpu_buffer_rsrc_t r = rsrc_dec(vg + (int64_t)t0 * p.k_st, ((int64_t)k1 - t0) * p.k_st * 2);
 #pragma unroll
-    for (int u = 0; u < LPT; ++u) {
-      const int row = u * RPL + lane / CPR;
+    for (int u = 0; u < LPW; ++u) {
+      const int span = wave * LPW + u;
+      const int row = span * RPL + lane / CPR;
       const int voff = (lane / CPR) * row_bytes + v_swz<D>(row, lane % CPR) * 16;
-      load_lds_b128_dec(r, tile + u * RPL * RB, voff, u * RPL * row_bytes);
+      load_lds_b128_dec(r, tile + span * RPL * RB, voff, span * RPL * row_bytes);
     }
+  };
+  auto vbuf = [&](auto bufc) -> unsigned char* {
+    constexpr int B = decltype(bufc)::value;
+    return B == 0 ? v_t0 : (B == 1 ? v_t1 : v_t2);
   };
   int v_roff[VB];
   {
@@ -160,12 +177,16 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
   // being read from the one a direct load is filling.
   auto tile = [&](auto bufc, int tt, bf16x8 (&kc)[KS], bf16x8 (&kn)[KS]) {
     constexpr int BUF = decltype(bufc)::value;
-    const unsigned char* cur = BUF ? v_t1 : v_t0;
+    const unsigned char* cur = vbuf(bufc);
     const int t0 = k0 + tt * BK;
     load_k(t0 + BK, kn);   // past the chunk's end: zeros, never used
-    load_v(BUF ? v_t0 : v_t1, t0 + BK);
-    wait_vmcnt<KS + LPT>();   // only the next tile's loads are outstanding: this tile's landed
-    __builtin_amdgcn_wave_barrier();
+    load_v(vbuf(std::integral_constant<int, (BUF + 1) % NB>{}), t0 + BK);
+    wait_vmcnt<KS + LPW>();   // only the next tile's loads are outstanding: this tile's landed
+    if constexpr (W > 1) {
+      asm volatile("s_barrier" ::: "memory");   // every wave's share of this tile has landed
+    } else {
+      __builtin_amdgcn_wave_barrier();
+    }
     f32x16 s;
 #pragma unroll
     for (int j = 0; j < 16; ++j) s[j] = 0.f;
@@ -222,7 +243,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
         __builtin_memcpy(&a, &both, sizeof a);
         oacc[vb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pk[kk], oacc[vb], 0, 0, 0);
       }
-    // every lane is done reading this V tile before the next iteration's copy overwrites it
+    // every lane is done reading this V tile before a later copy overwrites it
     __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0), vmcnt and expcnt not waited on
     __builtin_amdgcn_wave_barrier();
   };
@@ -232,9 +253,25 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
     load_k(k0, ka);
     load_v(v_t0, k0);
   }
-  for (int tt = 0; tt < n_tiles; tt += 2) {
-    tile(std::integral_constant<int, 0>{}, tt, ka, kb);
-    if (tt + 1 < n_tiles) tile(std::integral_constant<int, 1>{}, tt + 1, kb, ka);
+  // K alternates between two register sets, V between NB buffers: one period is 2 or 6 tiles
+  // (n_tiles is the same for every wave of the workgroup, so all reach the same barriers)
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  if constexpr (NB == 2) {
+    for (int tt = 0; tt < n_tiles; tt += 2) {
+      tile(I0{}, tt, ka, kb);
+      if (tt + 1 < n_tiles) tile(I1{}, tt + 1, kb, ka);
+    }
+  } else {
+    for (int tt = 0; tt < n_tiles; tt += 6) {
+      tile(I0{}, tt, ka, kb);
+      if (tt + 1 < n_tiles) tile(I1{}, tt + 1, kb, ka);
+      if (tt + 2 < n_tiles) tile(I2{}, tt + 2, ka, kb);
+      if (tt + 3 < n_tiles) tile(I0{}, tt + 3, kb, ka);
+      if (tt + 4 < n_tiles) tile(I1{}, tt + 4, ka, kb);
+      if (tt + 5 < n_tiles) tile(I2{}, tt + 5, kb, ka);
+    }
   }
   wait_vmcnt<0>();   // the last prefetch (zeros past the chunk) is not left in flight
 
@@ -349,20 +386,23 @@ hipError_t launch_combine(const CombineParams& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
-hipError_t launch_decode(const DecodeParams& p, int head_dim, hipStream_t stream) {
+hipError_t launch_decode(const DecodeParams& p, int head_dim, int waves, hipStream_t stream) {
   const int n_rg = (p.group * p.n_q + 31) / 32;
-  const int64_t grid = (int64_t)p.n_parts * n_rg * p.kv_heads * p.batch;
+  const int n_wg = (n_rg + waves - 1) / waves;
+  const int64_t grid = (int64_t)p.n_parts * n_wg * p.kv_heads * p.batch;
   if (grid == 0) return hipSuccess;
-  switch (head_dim) {
-    case 64:
-      hipLaunchKernelGGL(decode_kernel<64>, dim3((unsigned)grid), dim3(64), 0, stream, p);
-      break;
-    case 128:
-      hipLaunchKernelGGL(decode_kernel<128>, dim3((unsigned)grid), dim3(64), 0, stream, p);
-      break;
-    default:
-      return hipErrorInvalidValue;
+#define RA_DECODE_LAUNCH(DD, WW) \
+  hipLaunchKernelGGL((decode_kernel<DD, WW>), dim3((unsigned)grid), dim3(64 * WW), 0, stream, p)
+  switch (head_dim * 8 + waves) {
+    case 64 * 8 + 1: RA_DECODE_LAUNCH(64, 1); break;
+    case 64 * 8 + 2: RA_DECODE_LAUNCH(64, 2); break;
+    case 64 * 8 + 4: RA_DECODE_LAUNCH(64, 4); break;
+    case 128 * 8 + 1: RA_DECODE_LAUNCH(128, 1); break;
+    case 128 * 8 + 2: RA_DECODE_LAUNCH(128, 2); break;
+    case 128 * 8 + 4: RA_DECODE_LAUNCH(128, 4); break;
+    default: return hipErrorInvalidValue;
   }
+#undef RA_DECODE_LAUNCH
   return hipGetLastError();
 }
 

@@ -131,7 +131,8 @@ hipError_t launch_step_bf16(const StepParams& p, int head_dim, hipStream_t strea
 hipError_t launch_step_f32(const StepParams& p, int head_dim, hipStream_t stream);
 hipError_t launch_finalize(const FinalizeParams& p, hipStream_t stream);
 hipError_t launch_merge(const MergeParams& p, hipStream_t stream);
-hipError_t launch_decode(const DecodeParams& p, int head_dim, hipStream_t stream);
+// waves: 1, 2 or 4 row groups per workgroup sharing the chunk's tiles
+hipError_t launch_decode(const DecodeParams& p, int head_dim, int waves, hipStream_t stream);
 hipError_t launch_combine(const CombineParams& p, hipStream_t stream);
 hipError_t launch_bwd_prep(const BwdPrepParams& p, int head_dim, bool bf16, hipStream_t stream);
 hipError_t launch_bwd_step_f32(const BwdParams& p, int head_dim, hipStream_t stream);
