@@ -51,6 +51,9 @@ CASES = [
     (1, 4, 2, 6, 64, 600, CONTIG, 1, 100, 103),       # rows 0..2 see no key
     (1, 64, 8, 1, 128, 20000, NONE, 1, 0, 0),         # the long-context GQA head shape
     (1, 32, 32, 1, 128, 9000, CONTIG, 1, 9000, 0),    # MHA decode, whole block visible
+    (1, 16, 2, 16, 128, 3001, CONTIG, 1, 2985, 0),    # 128 packed rows: four waves share tiles
+    (1, 8, 2, 20, 64, 2000, NONE, 1, 0, 0),           # 80 packed rows: three waves and an idle one
+    (1, 8, 1, 20, 128, 1500, STRIPED, 4, 6003, 3),    # 160 packed rows: two four-wave workgroups
 ]
 
 
