@@ -465,7 +465,9 @@ int ra_decode_step(ra_state* st, const void* k, const void* v, int32_t kv_len, i
   if (!st) return fail(RA_E_INVALID, "state is NULL");
   if (st->finalized) return fail(RA_E_STATE, "step after finalize");
   const ra_desc* d = &st->desc;
-  if (d->dtype != RA_DTYPE_BF16) return fail(RA_E_UNSUPPORTED, "the split-KV step runs on bf16 inputs");
+  // fp32 inputs take the exactness path: the tiled fp32 step over the whole block
+  if (d->dtype == RA_DTYPE_F32 && mask_kind != RA_MASK_CAUSAL_ZIGZAG)
+    return ra_block_step(st, k, v, kv_len, mask_kind, q_offset, k_offset);
   if (mask_kind == RA_MASK_CAUSAL_ZIGZAG)
     return fail(RA_E_UNSUPPORTED, "the split-KV step takes single-range layouts (not zigzag)");
   ra_stats s;

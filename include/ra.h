@@ -212,8 +212,9 @@ size_t ra_decode_workspace_bytes(const ra_desc* desc, int32_t kv_len);
  * one wave.  Meant for short Q (decode, q_len up to a few tens); any q_len is accepted.
  * workspace: device, 256-byte aligned, at least ra_decode_workspace_bytes(desc, kv_len)
  * bytes (workspace_bytes says how many the caller passed); it holds the chunk states and is
- * free again once the enqueued work has completed.  Errors: RA_E_UNSUPPORTED for fp32 inputs
- * or RA_MASK_CAUSAL_ZIGZAG; RA_E_INVALID for a missing or short workspace and everything
+ * free again once the enqueued work has completed.  fp32 inputs take the exactness path: the
+ * call is ra_block_step's (the workspace is not used).  Errors: RA_E_UNSUPPORTED for
+ * RA_MASK_CAUSAL_ZIGZAG; RA_E_INVALID for a missing or short workspace and everything
  * ra_block_step rejects. */
 int ra_decode_step(ra_state* st, const void* k, const void* v, int32_t kv_len,
                    int32_t mask_kind, int64_t q_offset, int64_t k_offset, void* workspace,

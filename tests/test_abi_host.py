@@ -393,5 +393,7 @@ def test_decode_argument_validation():
     lib.ra_state_destroy(h)
     d32 = _desc(q_len=4, q_heads=8, kv_heads=2, dtype=ra.RA_DTYPE_F32)
     assert lib.ra_state_init(C.byref(d32), 0x10000, 0x20000, C.byref(h)) == ra.RA_OK
-    assert lib.ra_decode_step(h, K, V, 512, 0, 0, 0, ws, need) == ra.RA_E_UNSUPPORTED
+    # fp32 is the tiled step's: its checks, then (not run here) its launch
+    assert lib.ra_decode_step(h, None, V, 512, 0, 0, 0, None, 0) == E
+    assert lib.ra_decode_step(h, K, V, 512, ra.RA_MASK_CAUSAL_ZIGZAG, 0, 0, ws, need) == ra.RA_E_UNSUPPORTED
     lib.ra_state_destroy(h)

@@ -128,7 +128,7 @@ def test_decode_skips_and_empty_blocks():
     _check(o, lse, q, k, v, np.arange(n), np.arange(nk), False, "after skips O")
 
 
-def test_decode_rejects_short_workspace_and_fp32():
+def test_decode_rejects_short_workspace():
     import exact_long_context_amd as ra
     q, k, v = synth.random_case(830, 1, 4, 2, 1, 4096, 128, "bf16")
     qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
@@ -138,11 +138,21 @@ def test_decode_rejects_short_workspace_and_fp32():
     with pytest.raises(ra.RaError):
         st.decode_step(kd, vd, NONE, workspace=short)
     st.close()
-    q32, k32, v32 = (t.float().cuda() for t in (q, k, v))
-    st = ra.RingState(q32, k32)
-    with pytest.raises(ra.RaError):
-        st.decode_step(k32, v32, NONE)
+
+
+def test_decode_fp32_takes_the_exact_path():
+    """fp32 inputs go through the tiled fp32 step: the result meets the fp32 bar."""
+    import exact_long_context_amd as ra
+    from gpu_util import assert_f32_close
+    q, k, v = synth.random_case(831, 1, 8, 2, 3, 2000, 64, "f32")
+    qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+    st = ra.RingState(qd, kd)
+    st.decode_step(kd, vd, CONTIG, 1997, 0)
+    o, lse = st.finalize()
+    torch.cuda.synchronize()
     st.close()
+    ref, _ = oracle.dense_attention(to64(q), to64(k), to64(v), 1997 + np.arange(3), np.arange(2000), True)
+    assert_f32_close(to64(o), ref, "fp32 decode O")
 
 
 def test_decode_fullsize_million_keys_sampled_heads():
