@@ -236,7 +236,7 @@ def test_order_invariance_and_state_resume_bitwise():
     s = np.einsum("hid,htd->hit", to64(q)[0], np.repeat(to64(k)[0], 2, axis=0)) / math.sqrt(128)
     ok = oracle.allowed_mask(q_pos, np.arange(N), True)
     xmax = np.where(ok, s, -np.inf).max(axis=-1) * math.log2(math.e)
-    assert np.all(m[0] >= xmax - 8.0) and np.all(m[0] <= xmax + 1e-3)
+    assert np.all(m[0] >= xmax - 32.0) and np.all(m[0] <= xmax + 1e-3)
     st3.close()
 
 
@@ -317,3 +317,30 @@ def test_strided_views_without_copies():
     torch.cuda.synchronize()
     ref, _ = oracle.dense_attention(to64(q), to64(k), to64(v), q_pos, np.arange(N), True)
     assert_bf16_close(to64(o), ref, "token-major views")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_steps_are_bitwise_repeatable_across_many_workgroups(dtype):
+    """The same fresh step and resumed step, three times over: the state (m, l, O~) must be
+    bit-identical every time.  16384 rows x 16 heads fill the chip with co-resident
+    workgroups, so a race between workgroups or between the waves of one (a tile buffer reused
+    too early, a read not yet landed) shows up as rows that change from run to run."""
+    import exact_long_context_amd as ra
+    H, n, nk = 16, 16384, 320
+    g = torch.Generator(device="cpu").manual_seed(77)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    q = (torch.randn(1, H, n, 128, generator=g) * 0.3).to(tdt).cuda()
+    k = (torch.randn(1, H, 2 * nk, 128, generator=g) * 0.3).to(tdt).cuda()
+    v = torch.randn(1, H, 2 * nk, 128, generator=g).to(tdt).cuda()
+    say(f"  repeatability {dtype}: {H} heads x {n} rows, two blocks of {nk} keys")
+    states = []
+    for _ in range(3):
+        st = ra.RingState(q, k[:, :, :nk], ring_size=1)
+        st.step(k[:, :, :nk], v[:, :, :nk], NONE)
+        st.step(k[:, :, nk:], v[:, :, nk:], CONTIG, 10 * nk, 0)
+        torch.cuda.synchronize()
+        states.append(st.workspace.clone())
+        st.close()
+    for other in states[1:]:
+        diff = (states[0] != other).nonzero()
+        assert diff.numel() == 0, f"{diff.numel()} workspace bytes differ between identical runs"
