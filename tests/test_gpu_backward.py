@@ -163,3 +163,33 @@ def test_backward_full_size_sampled_rows_and_keys():
                                       q_pos[keys], True)
     assert_bf16_close(to64(dk0[:, :1, keys]), gk, "dK sampled keys")
     assert_bf16_close(to64(dv0[:, :1, keys]), gv, "dV sampled keys")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_backward_is_bitwise_repeatable(dtype):
+    """Three identical backward steps over 4096 rows x 8 heads (many workgroups on every CU):
+    dQ, dK and dV must be bit-identical every time, so no workgroup reads a buffer another one
+    is still writing."""
+    import exact_long_context_amd as ra
+    g = torch.Generator(device="cpu").manual_seed(79)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    H, n = 8, 4096
+    q = (torch.randn(1, H, n, 128, generator=g) * 0.3).to(tdt).cuda()
+    k = (torch.randn(1, H, n, 128, generator=g) * 0.3).to(tdt).cuda()
+    v = torch.randn(1, H, n, 128, generator=g).to(tdt).cuda()
+    dod = torch.randn(1, H, n, 128, generator=g).to(tdt).cuda()
+    o, lse, _ = lap_with_steps(q, [k], [v], 0, CONTIG, 1)
+    say(f"  backward repeatability {dtype}: {H} heads x {n} rows, causal diagonal block")
+    runs = []
+    for _ in range(3):
+        bw = ra.RingBackward(q, dod, o, lse, k, ring_size=1)
+        dk = torch.zeros(k.shape, dtype=torch.float32, device="cuda")
+        dv = torch.zeros(v.shape, dtype=torch.float32, device="cuda")
+        bw.step(k, v, dk, dv, CONTIG, 0, 0)
+        dq = bw.finalize()
+        torch.cuda.synchronize()
+        bw.close()
+        runs.append((dq.clone(), dk, dv))
+    for other in runs[1:]:
+        for a, b in zip(runs[0], other):
+            assert torch.equal(a, b)
