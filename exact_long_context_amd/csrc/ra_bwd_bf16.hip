@@ -175,7 +175,9 @@ void bwd_dq_kernel(BwdParams p) {
     qf[ks] = row_chunk(qrow + ks * 16, row_ok);
     dof[ks] = row_chunk(dorow + ks * 16, row_ok);
   }
-  const float lse2 = row_ok ? p.lse[srow] * kLog2e : -INFINITY;
+  // +inf for a row outside the launch or one that saw no key in the forward: 2^(x - lse) = 0
+  float lse2 = row_ok ? p.lse[srow] * kLog2e : INFINITY;
+  if (lse2 == -INFINITY) lse2 = INFINITY;
   const float Dr = row_ok ? p.D[srow] : 0.f;
   const float c2 = p.scale * kLog2e;
 
@@ -209,14 +211,22 @@ void bwd_dq_kernel(BwdParams p) {
       s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(map.rd(kt_b, ks), qf[ks], s, 0, 0, 0);
       dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(map.rd(vt_b, ks), dof[ks], dp, 0, 0, 0);
     }
-    // lane holds keys 8*(j/4) + 4*hi + (j%4) of this row
-    const int lim = min(row + p.diag, p.n_k - 1) - kt * BT - 4 * hi;
+    // lane holds keys 8*(j/4) + 4*hi + (j%4) of this row; the element mask only on tiles
+    // that cross the diagonal or the block's end for some row of the wave
     bf16x8 dsk[2];
+    if ((kt + 1) * BT - 1 <= i0 + wave * WR + p.diag && (kt + 1) * BT <= p.n_k) {
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const bool ok = (8 * (j >> 2) + (j & 3) <= lim) && lse2 != -INFINITY;
-      const float pr = ok ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[j], c2, -lse2)) : 0.f;
-      dsk[j >> 3][j & 7] = (__bf16)(pr * (dp[j] - Dr) * p.scale);
+      for (int j = 0; j < 16; ++j) {
+        const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[j], c2, -lse2));
+        dsk[j >> 3][j & 7] = (__bf16)(pr * (dp[j] - Dr) * p.scale);
+      }
+    } else {
+      const int lim = min(row + p.diag, p.n_k - 1) - kt * BT - 4 * hi;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const float pr = (8 * (j >> 2) + (j & 3) <= lim) ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[j], c2, -lse2)) : 0.f;
+        dsk[j >> 3][j & 7] = (__bf16)(pr * (dp[j] - Dr) * p.scale);
+      }
     }
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk)
@@ -344,7 +354,9 @@ void bwd_kv_kernel(BwdParams p) {
       const int i = r0 + tid;
       const bool ok = hh < p.group && i < p.n_q;
       const int64_t sr = ((int64_t)b * p.q_heads + h) * p.state_rows + i;
-      lse_t[buf][tid] = ok ? p.lse[sr] * kLog2e : -INFINITY;
+      // +inf for a row outside the launch or one that saw no key in the forward: 2^(x - lse) = 0
+      const float l2 = ok ? p.lse[sr] * kLog2e : INFINITY;
+      lse_t[buf][tid] = l2 == -INFINITY ? INFINITY : l2;
       if constexpr (DK) d_t[buf][tid] = ok ? p.D[sr] : 0.f;
     }
   };
@@ -374,7 +386,9 @@ void bwd_kv_kernel(BwdParams p) {
         for (int kh = 0; kh < KH; ++kh) dp[kh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa, vf[kh][ks], dp[kh], 0, 0, 0);
       }
     }
-    // lane holds key key[kh] against tile rows 8*(j/4) + 4*hi + (j%4)
+    // lane holds key key[kh] against tile rows 8*(j/4) + 4*hi + (j%4); a tile whose first
+    // row sees the wave's last key needs no element mask
+    const bool full = t0 + wave * KW + KW - 1 <= r0 + p.diag;
     const float4* lse4 = reinterpret_cast<const float4*>(&lse_t[B][0]);
     const float4* d4 = reinterpret_cast<const float4*>(&d_t[B][0]);
     bf16x8 wb[KH][2];   // P (MODE_DV) or dS (MODE_DK) in bf16, per key half and 16-row step
@@ -396,8 +410,10 @@ void bwd_kv_kernel(BwdParams p) {
         const int i = r0 + 8 * a + 4 * hi + c;
 #pragma unroll
         for (int kh = 0; kh < KH; ++kh) {
-          const bool ok = key_ok[kh] && i < p.n_q && key[kh] <= i + p.diag && lv[c] != -INFINITY;
-          const float pr = ok ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[kh][j], c2, -lv[c])) : 0.f;
+          // rows past the launch carry lse = +inf (p = 0) and keys past the block only feed
+          // their own, unstored, column: only the causal diagonal needs the element mask
+          const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kh][j], c2, -lv[c]));
+          const float pr = (full || key[kh] <= i + p.diag) ? e : 0.f;
           if constexpr (DK)
             wb[kh][j >> 3][j & 7] = (__bf16)(pr * (dp[kh][j] - dvv[c]) * p.scale);
           else
