@@ -46,7 +46,6 @@ typedef __attribute__((address_space(3))) void lds_void;
 constexpr int NT = 256;     // 4 waves
 constexpr int WR = 32;      // rows (dq) or keys (dkdv) per wave
 constexpr int BO = 4 * WR;  // owned per workgroup
-constexpr int BT = 32;      // streamed tile rows
 constexpr float kLog2e = 1.4426950408889634f;
 
 // physical 16-byte chunk of logical chunk c of tile row t
@@ -72,7 +71,7 @@ using ic = std::integral_constant<int, N>;
 // tile (k_roff: row r32, chunk 2*ks + hi) and where its transposing reads go (t_roff: rows
 // 4*(g>>1) + e (+8 for the second half, +16*kk as an immediate), columns 32*vb + 16*(g&1) +
 // 4*a), and which global chunk it fetches for each direct load.
-template <int D>
+template <int D, int BT>
 struct TileMap {
   static constexpr int KS = D / 16, VB = D / 32, RB = D * 2, CPR = D / 8, RPL = 64 / CPR;
   static constexpr int LPW = BT * RB / 1024 / 4;
@@ -109,8 +108,9 @@ struct TileMap {
       load_lds_b128_bwd(r, tile + row0 * RB, goff[u], row0 * row_bytes);
     }
   }
-  __device__ bf16x8 rd(const unsigned char* tile, int ks) const {
-    return *reinterpret_cast<const bf16x8*>(tile + k_roff[ks]);
+  // operand chunk ks of tile row half * 32 + r32
+  __device__ bf16x8 rd(const unsigned char* tile, int ks, int half = 0) const {
+    return *reinterpret_cast<const bf16x8*>(tile + k_roff[ks] + half * 32 * RB);
   }
   __device__ bf16x8 rd_t(const unsigned char* tile, int kk, int vb) const {
     const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(tile + t_roff[0][vb] + kk * 16 * RB));
@@ -134,10 +134,11 @@ __device__ __forceinline__ bf16x8 row_chunk(const __bf16* p, bool ok) {
 }
 
 // ------------------------------------------------------------------------------------------
-template <int D>
+template <int D, int BT>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void bwd_dq_kernel(BwdParams p) {
-  using M = TileMap<D>;
+  using M = TileMap<D, BT>;
+  constexpr int NH = BT / 32;   // 32-key halves of a streamed tile
   constexpr int KS = M::KS, VB = M::VB, RB = M::RB;
   __shared__ __attribute__((aligned(16))) unsigned char k_t0[BT * RB];
   __shared__ __attribute__((aligned(16))) unsigned char k_t1[BT * RB];
@@ -200,36 +201,45 @@ void bwd_dq_kernel(BwdParams p) {
     map.load(v_tiles[1 - B], vg, (int64_t)(kt + 1) * BT, p.n_k, p.k_st, wave, row_bytes);
     const unsigned char* kt_b = k_tiles[B];
     const unsigned char* vt_b = v_tiles[B];
-    f32x16 s, dp;
+    f32x16 s[NH], dp[NH];
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      s[j] = 0.f;
-      dp[j] = 0.f;
-    }
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(map.rd(kt_b, ks), qf[ks], s, 0, 0, 0);
-      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(map.rd(vt_b, ks), dof[ks], dp, 0, 0, 0);
-    }
-    // lane holds keys 8*(j/4) + 4*hi + (j%4) of this row; the element mask only on tiles
-    // that cross the diagonal or the block's end for some row of the wave
-    bf16x8 dsk[2];
-    if ((kt + 1) * BT - 1 <= i0 + wave * WR + p.diag && (kt + 1) * BT <= p.n_k) {
+    for (int kh = 0; kh < NH; ++kh)
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
-        const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[j], c2, -lse2));
-        dsk[j >> 3][j & 7] = (__bf16)(pr * (dp[j] - Dr) * p.scale);
+        s[kh][j] = 0.f;
+        dp[kh][j] = 0.f;
       }
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int kh = 0; kh < NH; ++kh) {
+        s[kh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(map.rd(kt_b, ks, kh), qf[ks], s[kh], 0, 0, 0);
+        dp[kh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(map.rd(vt_b, ks, kh), dof[ks], dp[kh], 0, 0, 0);
+      }
+    // lane holds keys 32*kh + 8*(j/4) + 4*hi + (j%4) of this row; the element mask only on
+    // tiles that cross the diagonal or the block's end for some row of the wave
+    bf16x8 dsk[2 * NH];
+    if ((kt + 1) * BT - 1 <= i0 + wave * WR + p.diag && (kt + 1) * BT <= p.n_k) {
+#pragma unroll
+      for (int kh = 0; kh < NH; ++kh)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kh][j], c2, -lse2));
+          dsk[2 * kh + (j >> 3)][j & 7] = (__bf16)(pr * (dp[kh][j] - Dr) * p.scale);
+        }
     } else {
       const int lim = min(row + p.diag, p.n_k - 1) - kt * BT - 4 * hi;
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const float pr = (8 * (j >> 2) + (j & 3) <= lim) ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[j], c2, -lse2)) : 0.f;
-        dsk[j >> 3][j & 7] = (__bf16)(pr * (dp[j] - Dr) * p.scale);
-      }
+      for (int kh = 0; kh < NH; ++kh)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const bool ok = 32 * kh + 8 * (j >> 2) + (j & 3) <= lim;
+          const float pr = ok ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[kh][j], c2, -lse2)) : 0.f;
+          dsk[2 * kh + (j >> 3)][j & 7] = (__bf16)(pr * (dp[kh][j] - Dr) * p.scale);
+        }
     }
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk)
+    for (int kk = 0; kk < 2 * NH; ++kk)
 #pragma unroll
       for (int vb = 0; vb < VB; ++vb)
         dq[vb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(map.rd_t(kt_b, kk, vb), dsk[kk], dq[vb], 0, 0, 0);
@@ -275,14 +285,17 @@ constexpr int MODE_DV = 0, MODE_DK = 1;
 // waves per SIMD is faster for both modes (dV 10.4 ms -> see the design notes).
 template <int MODE>
 constexpr int kv_halves() { return 1; }
+// streamed tile rows of each kernel (32 or 64)
+constexpr int kBwdTileDq = 64, kBwdTileDv = 64, kBwdTileDk = 32;
 
-template <int D, int MODE>
+template <int D, int MODE, int BT>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(3 - kv_halves<MODE>(), 3 - kv_halves<MODE>())))
 void bwd_kv_kernel(BwdParams p) {
   constexpr int KH = kv_halves<MODE>();
   constexpr int KW = 32 * KH;   // keys per wave
   constexpr int KO = 4 * KW;    // keys per workgroup
-  using M = TileMap<D>;
+  constexpr int NH = BT / 32;   // 32-row halves of a streamed tile
+  using M = TileMap<D, BT>;
   constexpr int KS = M::KS, VB = M::VB, RB = M::RB;
   constexpr bool DK = MODE == MODE_DK;
   __shared__ __attribute__((aligned(16))) unsigned char q_t0[BT * RB];
@@ -367,63 +380,69 @@ void bwd_kv_kernel(BwdParams p) {
     const int r0 = r_start + (u % n_rt) * BT;
     const unsigned char* qt_b = q_tiles[B];
     const unsigned char* ot_b = o_tiles[B];
-    f32x16 s[KH], dp[KH];
+    f32x16 s[KH][NH], dp[KH][DK ? NH : 1];
 #pragma unroll
     for (int kh = 0; kh < KH; ++kh)
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        s[kh][j] = 0.f;
-        dp[kh][j] = 0.f;
+      for (int rh = 0; rh < NH; ++rh)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          s[kh][rh][j] = 0.f;
+          if constexpr (DK) dp[kh][rh][j] = 0.f;
+        }
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int rh = 0; rh < NH; ++rh) {
+        const bf16x8 qa = map.rd(qt_b, ks, rh);
+#pragma unroll
+        for (int kh = 0; kh < KH; ++kh) s[kh][rh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[kh][ks], s[kh][rh], 0, 0, 0);
+        if constexpr (DK) {
+          const bf16x8 oa = map.rd(ot_b, ks, rh);
+#pragma unroll
+          for (int kh = 0; kh < KH; ++kh) dp[kh][rh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa, vf[kh][ks], dp[kh][rh], 0, 0, 0);
+        }
       }
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const bf16x8 qa = map.rd(qt_b, ks);
-#pragma unroll
-      for (int kh = 0; kh < KH; ++kh) s[kh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[kh][ks], s[kh], 0, 0, 0);
-      if constexpr (DK) {
-        const bf16x8 oa = map.rd(ot_b, ks);
-#pragma unroll
-        for (int kh = 0; kh < KH; ++kh) dp[kh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa, vf[kh][ks], dp[kh], 0, 0, 0);
-      }
-    }
-    // lane holds key key[kh] against tile rows 8*(j/4) + 4*hi + (j%4); a tile whose first
-    // row sees the wave's last key needs no element mask
+    // lane holds key key[kh] against tile rows 32*rh + 8*(j/4) + 4*hi + (j%4); a tile whose
+    // first row sees the wave's last key needs no element mask
     const bool full = t0 + wave * KW + KW - 1 <= r0 + p.diag;
     const float4* lse4 = reinterpret_cast<const float4*>(&lse_t[B][0]);
     const float4* d4 = reinterpret_cast<const float4*>(&d_t[B][0]);
-    bf16x8 wb[KH][2];   // P (MODE_DV) or dS (MODE_DK) in bf16, per key half and 16-row step
+    bf16x8 wb[KH][2 * NH];   // P (MODE_DV) or dS (MODE_DK) in bf16, per key half and 16-row step
 #pragma unroll
-    for (int a = 0; a < 4; ++a) {
-      const float4 l4 = lse4[2 * a + hi];   // rows 8a + 4hi .. +3
-      const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
-      float dvv[4] = {0.f, 0.f, 0.f, 0.f};
-      if constexpr (DK) {
-        const float4 dd = d4[2 * a + hi];
-        dvv[0] = dd.x;
-        dvv[1] = dd.y;
-        dvv[2] = dd.z;
-        dvv[3] = dd.w;
-      }
+    for (int rh = 0; rh < NH; ++rh)
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const int j = 4 * a + c;
-        const int i = r0 + 8 * a + 4 * hi + c;
+      for (int a = 0; a < 4; ++a) {
+        const float4 l4 = lse4[8 * rh + 2 * a + hi];   // rows 32rh + 8a + 4hi .. +3
+        const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+        float dvv[4] = {0.f, 0.f, 0.f, 0.f};
+        if constexpr (DK) {
+          const float4 dd = d4[8 * rh + 2 * a + hi];
+          dvv[0] = dd.x;
+          dvv[1] = dd.y;
+          dvv[2] = dd.z;
+          dvv[3] = dd.w;
+        }
 #pragma unroll
-        for (int kh = 0; kh < KH; ++kh) {
-          // rows past the launch carry lse = +inf (p = 0) and keys past the block only feed
-          // their own, unstored, column: only the causal diagonal needs the element mask
-          const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kh][j], c2, -lv[c]));
-          const float pr = (full || key[kh] <= i + p.diag) ? e : 0.f;
-          if constexpr (DK)
-            wb[kh][j >> 3][j & 7] = (__bf16)(pr * (dp[kh][j] - dvv[c]) * p.scale);
-          else
-            wb[kh][j >> 3][j & 7] = (__bf16)pr;
+        for (int c = 0; c < 4; ++c) {
+          const int j = 4 * a + c;
+          const int i = r0 + 32 * rh + 8 * a + 4 * hi + c;
+#pragma unroll
+          for (int kh = 0; kh < KH; ++kh) {
+            // rows past the launch carry lse = +inf (p = 0) and keys past the block only feed
+            // their own, unstored, column: only the causal diagonal needs the element mask
+            const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kh][rh][j], c2, -lv[c]));
+            const float pr = (full || key[kh] <= i + p.diag) ? e : 0.f;
+            if constexpr (DK)
+              wb[kh][2 * rh + (j >> 3)][j & 7] = (__bf16)(pr * (dp[kh][rh][j] - dvv[c]) * p.scale);
+            else
+              wb[kh][2 * rh + (j >> 3)][j & 7] = (__bf16)pr;
+          }
         }
       }
-    }
     const unsigned char* tr_tile = DK ? qt_b : ot_b;   // dK: Q^T dS; dV: dO^T P
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk)
+    for (int kk = 0; kk < 2 * NH; ++kk)
 #pragma unroll
       for (int vb = 0; vb < VB; ++vb) {
         const bf16x8 ta = map.rd_t(tr_tile, kk, vb);
@@ -468,9 +487,9 @@ hipError_t launch_d(const BwdParams& p, hipStream_t stream) {
   const int64_t gq = (int64_t)((p.n_q + BO - 1) / BO) * p.q_heads * p.batch;
   const int64_t gv = (int64_t)((p.n_k + 128 * kv_halves<MODE_DV>() - 1) / (128 * kv_halves<MODE_DV>())) * p.kv_heads * p.batch;
   const int64_t gk = (int64_t)((p.n_k + 128 * kv_halves<MODE_DK>() - 1) / (128 * kv_halves<MODE_DK>())) * p.kv_heads * p.batch;
-  if (gq > 0) hipLaunchKernelGGL((bwd_dq_kernel<D>), dim3((unsigned)gq), dim3(NT), 0, stream, p);
-  if (gv > 0) hipLaunchKernelGGL((bwd_kv_kernel<D, MODE_DV>), dim3((unsigned)gv), dim3(NT), 0, stream, p);
-  if (gk > 0) hipLaunchKernelGGL((bwd_kv_kernel<D, MODE_DK>), dim3((unsigned)gk), dim3(NT), 0, stream, p);
+  if (gq > 0) hipLaunchKernelGGL((bwd_dq_kernel<D, kBwdTileDq>), dim3((unsigned)gq), dim3(NT), 0, stream, p);
+  if (gv > 0) hipLaunchKernelGGL((bwd_kv_kernel<D, MODE_DV, kBwdTileDv>), dim3((unsigned)gv), dim3(NT), 0, stream, p);
+  if (gk > 0) hipLaunchKernelGGL((bwd_kv_kernel<D, MODE_DK, kBwdTileDk>), dim3((unsigned)gk), dim3(NT), 0, stream, p);
   return hipGetLastError();
 }
 
