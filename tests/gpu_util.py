@@ -71,9 +71,22 @@ def bf16_errors(got: np.ndarray, ref: np.ndarray) -> dict:
     }
 
 
-def assert_bf16_close(got, ref, what=""):
+# per-row bound of our own for outputs: ||err_row|| <= BF16_ROWWISE * ||ref_row|| + 1e-6, so
+# that a few wrong rows cannot hide inside whole-tensor norms (rows are the last axis)
+BF16_ROWWISE = 2e-2
+
+
+def assert_bf16_close(got, ref, what="", rowwise=BF16_ROWWISE):
     e = bf16_errors(got, ref)
-    say(f"    {what} max_abs={e['max_abs']:.3e} mean_abs={e['mean_abs']:.3e} normwise={e['normwise']:.3e}")
+    msg = f"    {what} max_abs={e['max_abs']:.3e} mean_abs={e['mean_abs']:.3e} normwise={e['normwise']:.3e}"
+    if rowwise is not None and np.asarray(ref).size:
+        g = np.asarray(got, dtype=np.float64).reshape(-1, np.shape(ref)[-1])
+        r = np.asarray(ref, dtype=np.float64).reshape(-1, np.shape(ref)[-1])
+        row = np.linalg.norm(g - r, axis=1) / (np.linalg.norm(r, axis=1) + 1e-6 / rowwise)
+        e["worst_row"] = float(row.max())
+        msg += f" worst_row={e['worst_row']:.3e}"
+        assert e["worst_row"] <= rowwise, (what, e, int(row.argmax()))
+    say(msg)
     assert e["max_abs"] <= BF16_MAX_ABS, (what, e)
     assert e["mean_abs"] <= BF16_MEAN_ABS, (what, e)
     assert e["normwise"] <= BF16_NORMWISE, (what, e)
