@@ -201,3 +201,21 @@ def test_decode_is_bitwise_repeatable():
         st.close()
     for other in states[1:]:
         assert torch.equal(states[0], other)
+
+
+def test_decode_token_major_views():
+    """Q, K and V as token-major [B, n, H, d] storage seen through [B, H, n, d] views (the
+    strides go through the ABI; nothing is copied)."""
+    import exact_long_context_amd as ra
+    B, Hq, Hkv, n, d, nk = 2, 16, 4, 3, 128, 2500
+    q, k, v = synth.random_case(840, B, Hq, Hkv, n, nk, d, "bf16")
+    qt = q.permute(0, 2, 1, 3).contiguous().cuda().permute(0, 2, 1, 3)
+    kt = k.permute(0, 2, 1, 3).contiguous().cuda().permute(0, 2, 1, 3)
+    vt = v.permute(0, 2, 1, 3).contiguous().cuda().permute(0, 2, 1, 3)
+    assert kt.stride()[2] == Hkv * d and not kt.is_contiguous()
+    st = ra.RingState(qt, kt)
+    st.decode_step(kt, vt, CONTIG, nk - n, 0)
+    o, lse = st.finalize()
+    torch.cuda.synchronize()
+    st.close()
+    _check(o, lse, q, k, v, nk - n + np.arange(n), np.arange(nk), True, "token-major decode O")
