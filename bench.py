@@ -322,6 +322,9 @@ def main() -> int:
     per_step_ms = [[evs[2 * s].elapsed_time(evs[2 * s + 1]) for s in range(w.P)] for evs in events]
     # end of step s-1 to start of step s: launch gap plus any wait for the block's transfer
     gaps_ms = [[evs[2 * s - 1].elapsed_time(evs[2 * s]) for s in range(1, w.P)] for evs in events]
+    # each timed lap from its first step's start to its last step's end (init and finalize,
+    # ~0.1 ms, fall outside)
+    lap_span_ms = sorted(evs[0].elapsed_time(evs[2 * w.P - 1]) for evs in events)
     live_steps = [s for s in range(w.P) if step_flops[s] > 0]
     kern_ms = sum(per_step_ms[i][s] for i in range(args.steps) for s in live_steps)
     kern_launches = len(live_steps) * args.steps
@@ -380,6 +383,8 @@ def main() -> int:
             "blocks_run": stats["blocks_run"], "blocks_skipped": stats["blocks_skipped"],
             "tiles": {"full": stats["tiles_full"], "partial": stats["tiles_partial"],
                       "empty": stats["tiles_empty"], "tile_q": stats["tile_q"], "tile_k": stats["tile_k"]},
+            "lap_steps_ms_median": round(lap_span_ms[len(lap_span_ms) // 2], 4),
+            "lap_steps_ms_min": round(lap_span_ms[0], 4),
             "step_kernel_ms_median": [round(sorted(col)[len(col) // 2], 4) for col in zip(*per_step_ms)],
             "gap_before_step_ms_median": [round(sorted(col)[len(col) // 2], 4) for col in zip(*gaps_ms)],
             "peak_mem_gib": round(torch.cuda.max_memory_allocated() / 2**30, 2),
