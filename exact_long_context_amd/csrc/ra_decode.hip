@@ -52,8 +52,11 @@ __device__ __forceinline__ int v_swz(int t, int c) {
   else return c ^ (4 * ((t >> 1) & 1));
 }
 
+// V is read exactly once and each copy instruction covers whole 1 KB spans, so it goes with
+// the nontemporal bit (cache policy 2): streamed past the L2 instead of filling it.  K keeps
+// the default policy: its register loads touch each 128-byte line over several instructions.
 __device__ __forceinline__ void load_lds_b128_dec(__amdgpu_buffer_rsrc_t r, void* lds, int voff, int soff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 16, voff, soff, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 16, voff, soff, 0, 2);
 }
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_dec(const void* base, int64_t bytes) {
