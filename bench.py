@@ -101,6 +101,72 @@ def cpu_baseline(w, rank: int, q, k, v, seconds: float):
     }
 
 
+def host_threads() -> int:
+    try:
+        from threadpoolctl import threadpool_info
+        return max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        return len(os.sched_getaffinity(0))
+
+
+def cpu_backward_baseline(w, rank: int, j: int, q, kb, vb, d_out, seconds: float):
+    """Time the fp64 oracle's backward step (oracle.backward_block) on this host: query head 0,
+    whole chunks of local rows against all keys of block j, until `seconds` of timed work.
+    Its inputs lse and D for those rows come from the oracle's own forward against that block
+    (untimed).  Useful flops as on the GPU: 10*d per allowed pair."""
+    import numpy as np
+    import oracle
+    causal = w.mask != "none"
+    q_pos = oracle.tokens_of_rank(w.N, w.P, w.layout, rank)
+    k_pos = oracle.tokens_of_rank(w.N, w.P, w.layout, j)
+    k64 = kb[j][0:1, 0:1].double().cpu().numpy()
+    v64 = vb[j][0:1, 0:1].double().cpu().numpy()
+    chunk, done, flops, timed = 512, 0, 0, 0.0
+    while done < w.n_local and timed < seconds:
+        rows = np.arange(done, min(done + chunk, w.n_local))
+        q64 = q[0:1, 0:1, done:done + rows.size].double().cpu().numpy()
+        do64 = d_out[0:1, 0:1, done:done + rows.size].double().cpu().numpy()
+        o, lse = oracle.dense_attention(q64, k64, v64, q_pos[rows], k_pos, causal)
+        D = oracle.backward_row_terms(do64, o)
+        t0 = time.perf_counter()
+        oracle.backward_block(q64, k64, v64, do64, lse, D, q_pos[rows], k_pos, causal)
+        timed += time.perf_counter() - t0
+        flops += 10 * w.head_dim * oracle.live_pair_count(q_pos[rows], k_pos, causal)
+        done += rows.size
+    return {"value": round(flops / timed / 1e12, 5) if timed > 0 else 0.0, "unit": "TFLOP/s",
+            "cores": host_threads(), "kind": "oracle",
+            "sample": (f"fp64 oracle.backward_block of query head 0, local rows 0..{done - 1} of rank {rank} "
+                       f"against the {k_pos.size} keys of block {j}, {timed:.1f} s timed; 10*d flops per allowed pair"),
+            "seconds": round(timed, 3)}
+
+
+def cpu_decode_baseline(seconds: float):
+    """Time the fp64 oracle's block update (oracle.online_block_update) for one decode token of
+    64 query heads over 8 KV heads (d = 128) against a 16K-key block on this host, repeated
+    until `seconds`; reported in the decode unit, bf16 K+V bytes of the block per second."""
+    import numpy as np
+    import oracle
+    import synth
+    B, Hq, Hkv, d, nk = 1, 64, 8, 128, 16384
+    sc = 1 / math.sqrt(128)
+    q = synth.round_to_dtype(synth.draw(5, synth.Q_ID, 0, B, Hq, 1, d, sc), "bf16").double().numpy()
+    k = synth.round_to_dtype(synth.draw(5, synth.K_ID, -1, B, Hkv, nk, d, sc), "bf16").double().numpy()
+    v = synth.round_to_dtype(synth.draw(5, synth.V_ID, -1, B, Hkv, nk, d, sc), "bf16").double().numpy()
+    st = oracle.online_state_init(B, Hq, 1, d)
+    q_pos, k_pos = np.array([nk - 1]), np.arange(nk)
+    calls, t0 = 0, time.perf_counter()
+    while calls == 0 or time.perf_counter() - t0 < seconds:
+        oracle.online_block_update(st, q, k, v, q_pos, k_pos, False)
+        calls += 1
+    el = time.perf_counter() - t0
+    kv_bytes = 2 * B * Hkv * nk * d * 2
+    return {"value": round(kv_bytes * calls / el / 1e9, 3), "unit": "GB/s",
+            "cores": host_threads(), "kind": "oracle",
+            "sample": (f"fp64 oracle.online_block_update, 1 token x 64 query heads over 8 KV heads against "
+                       f"{nk} keys, {calls} calls in {el:.1f} s; K+V bytes as bf16"),
+            "seconds": round(el, 3)}
+
+
 def hbm_passes(ra, q, k, v, ws, w, desc, reps: int = 20):
     """The HBM-bound passes beside the lap: finalize over the lap's state, and block steps
     with short KV blocks (the state read and write then outweigh the MFMA work).  Each is
@@ -153,7 +219,7 @@ def hbm_passes(ra, q, k, v, ws, w, desc, reps: int = 20):
     return res
 
 
-def decode_passes(ra, reps: int = 20):
+def decode_passes(ra, reps: int = 20, cpu_seconds: float = 0.0):
     """The split-KV block step (ra_decode_step) for few query rows of the long-context GQA
     head shape (64 query heads over 8 KV heads, d = 128, bf16): one block of n_k keys per call
     into a resumed state, for blocks from one ring block (16K keys) to the whole 1M-token
@@ -175,7 +241,7 @@ def decode_passes(ra, reps: int = 20):
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / reps
 
-    for n_q in (1, 8):
+    for n_q in (1, 8, 16):
         q = synth.draw_device(5, synth.Q_ID, 0, B, Hq, n_q, d, 1 / math.sqrt(128), "bf16", "cuda")
         for nk in (16384, 131072, 1048576):
             k = synth.draw_device(5, synth.K_ID, -1, B, Hkv, nk, d, 1 / math.sqrt(128), "bf16", "cuda")
@@ -195,10 +261,13 @@ def decode_passes(ra, reps: int = 20):
                 "frac_of_8TB_s": round(nbytes / ms / 1e6 / PEAK_HBM_GBS, 3),
                 "tiled_step_ms": round(ms_tiled, 4), "speedup_vs_tiled": round(ms_tiled / ms, 2)}
             del k, v, ws
+    if cpu_seconds > 0:
+        log("[bench] timing the oracle decode update on host cores")
+        res["cpu_oracle"] = cpu_decode_baseline(cpu_seconds)
     return res
 
 
-def backward_lap(ra, q, kb, vb, out, lse, w, rank, mask, order, step_flops, laps):
+def backward_lap(ra, q, kb, vb, out, lse, w, rank, mask, order, step_flops, laps, cpu_seconds=0.0):
     """Time the backward lap: ra_bwd_init, one ra_bwd_block_step per block in ring order
     (each block's dK, dV accumulating in its own buffer), ra_bwd_finalize.  Useful flops:
     10*d per allowed pair (the five products of the standard backward: the recomputed scores,
@@ -229,9 +298,13 @@ def backward_lap(ra, q, kb, vb, out, lse, w, rank, mask, order, step_flops, laps
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / laps
     flops = sum(step_flops) // 4 * 10      # 10*d per pair (step_flops holds 4*d per pair)
-    return {"ms_per_lap": round(ms, 4), "useful_flops_per_lap": flops,
-            "TFLOP_s": round(flops / ms / 1e9, 1), "pct_of_peak": round(flops / ms / 1e9 / PEAK_BF16_TFLOPS * 100, 2),
-            "flop_convention": "10*d per allowed pair per query head"}
+    res = {"ms_per_lap": round(ms, 4), "useful_flops_per_lap": flops,
+           "TFLOP_s": round(flops / ms / 1e9, 1), "pct_of_peak": round(flops / ms / 1e9 / PEAK_BF16_TFLOPS * 100, 2),
+           "flop_convention": "10*d per allowed pair per query head"}
+    if cpu_seconds > 0:
+        log("[bench] timing the oracle backward on host cores")
+        res["cpu_oracle"] = cpu_backward_baseline(w, rank, order[0], q, kb, vb, d_out, cpu_seconds)
+    return res
 
 
 def main() -> int:
@@ -345,9 +418,10 @@ def main() -> int:
     }
 
     hbm = hbm_passes(ra, qd, kb[0], vb[0], ws, w, desc) if args.hbm_passes else None
-    bwd = backward_lap(ra, qd, kb, vb, out, lse, w, rank, mask, order, step_flops, args.steps) \
+    side_cpu = 0.0 if args.no_cpu_baseline else 5.0
+    bwd = backward_lap(ra, qd, kb, vb, out, lse, w, rank, mask, order, step_flops, args.steps, side_cpu) \
         if args.backward else None
-    dec = decode_passes(ra) if args.decode else None
+    dec = decode_passes(ra, cpu_seconds=side_cpu) if args.decode else None
 
     cpu = None
     if not args.no_cpu_baseline:

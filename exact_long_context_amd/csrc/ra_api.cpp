@@ -245,10 +245,12 @@ int make_state(const ra_desc* d, const void* q, void* ws, int fresh, ra_state** 
   return RA_OK;
 }
 
-// The split-KV step: enough key chunks that the whole chip streams the block (about two
-// waves per SIMD of 256 compute units), none shorter than kDecodeMinChunk keys so that a
-// wave's fixed cost stays small next to its loads.
+// The split-KV step: enough key chunks that the whole chip streams the block, none shorter
+// than kDecodeMinChunk keys per wave so that a wave's fixed cost stays small next to its
+// loads.  decode_kernel aims at 2048 waves (two per SIMD); decode_ring_kernel's four-wave
+// workgroups hold an 80 KB LDS ring each and aim at 512 of them (two per CU).
 constexpr int64_t kDecodeTargetWaves = 2048;
+constexpr int64_t kDecodeTargetRings = 512;
 constexpr int32_t kDecodeMinChunk = 256;
 
 struct DecodePlan {
@@ -260,14 +262,22 @@ int64_t decode_row_groups(const ra_desc* d) {
   return (packed + ra::kDecodeRows - 1) / ra::kDecodeRows;
 }
 
-DecodePlan decode_plan(const ra_desc* d, int32_t n_keys) {
+// key chunks wanted per (batch, KV head, workgroup of row groups)
+int64_t decode_want(const ra_desc* d, ra::DecodeShape sh) {
+  const int64_t n_wg = (decode_row_groups(d) + sh.R - 1) / sh.R;
+  const int64_t base = (int64_t)d->batch * d->kv_heads * n_wg * (sh.ring ? 1 : sh.R);
+  const int64_t target = sh.ring ? kDecodeTargetRings : kDecodeTargetWaves;
+  return base >= target ? 1 : (target + base - 1) / base;
+}
+
+DecodePlan decode_plan(const ra_desc* d, ra::DecodeShape sh, int32_t n_keys) {
   DecodePlan pl{0, 0};
   if (n_keys <= 0) return pl;
-  const int64_t base = (int64_t)d->batch * d->kv_heads * decode_row_groups(d);
-  const int64_t want = base >= kDecodeTargetWaves ? 1 : (kDecodeTargetWaves + base - 1) / base;
+  const int64_t want = decode_want(d, sh);
+  const int64_t step = (int64_t)ra::kDecodeTileK * sh.S;
   int64_t chunk = (n_keys + want - 1) / want;
-  chunk = (chunk + ra::kDecodeTileK - 1) / ra::kDecodeTileK * ra::kDecodeTileK;
-  if (chunk < kDecodeMinChunk) chunk = kDecodeMinChunk;
+  chunk = (chunk + step - 1) / step * step;
+  if (chunk < (int64_t)kDecodeMinChunk * sh.S) chunk = (int64_t)kDecodeMinChunk * sh.S;
   pl.chunk = (int32_t)chunk;
   pl.n_parts = (int32_t)((n_keys + chunk - 1) / chunk);
   return pl;
@@ -277,20 +287,29 @@ struct DecodeLayout {
   size_t o_off, m_off, l_off, total;
 };
 
-// Parts of a block of kv_len keys are at most decode_plan(kv_len)'s: a causal block only
-// ever plans over fewer keys, and fewer keys never give more parts (n_parts <= want and
-// n_parts <= ceil(keys / kDecodeMinChunk), both bounds non-decreasing in the key count).
+// Partial states of a block of kv_len keys.  A causal block plans over its visible keys
+// n_keys <= kv_len, and the shape may change with n_keys (two row groups), so the bound is the
+// larger over the shapes n_keys can take.  For one shape, n_parts <= want and
+// n_parts <= ceil(n_keys / (S * kDecodeMinChunk)), both non-decreasing in n_keys, and each
+// part leaves S partial states.
 DecodeLayout decode_layout(const ra_desc* d, int32_t kv_len) {
-  const int64_t base = (int64_t)d->batch * d->kv_heads * decode_row_groups(d);
-  const int64_t want = base >= kDecodeTargetWaves ? 1 : (kDecodeTargetWaves + base - 1) / base;
-  int64_t parts = ((int64_t)kv_len + kDecodeMinChunk - 1) / kDecodeMinChunk;
-  if (parts > want) parts = want;
+  const int64_t n_rg = decode_row_groups(d);
+  auto bound = [&](ra::DecodeShape sh) {
+    int64_t parts = ((int64_t)kv_len + sh.S * kDecodeMinChunk - 1) / (sh.S * kDecodeMinChunk);
+    const int64_t want = decode_want(d, sh);
+    return (parts > want ? want : parts) * sh.S;
+  };
+  int64_t parts = bound(ra::decode_shape(n_rg, kv_len));
+  if (n_rg == 2) {
+    const int64_t p2 = bound(ra::decode_shape(n_rg, 0));
+    if (p2 > parts) parts = p2;
+  }
   const size_t rows = (size_t)d->batch * d->q_heads * d->q_len;
   DecodeLayout L;
   L.o_off = 0;
   L.m_off = align256((size_t)parts * rows * d->head_dim * sizeof(float));
   L.l_off = L.m_off + align256((size_t)parts * rows * sizeof(float));
-  L.total = rows && parts ? L.l_off + align256((size_t)parts * rows * sizeof(float)) : 0;
+  L.total = rows && parts && kv_len > 0 ? L.l_off + align256((size_t)parts * rows * sizeof(float)) : 0;
   return L;
 }
 
@@ -494,10 +513,13 @@ int ra_decode_step(ra_state* st, const void* k, const void* v, int32_t kv_len, i
   // keys past the last row's causal limit are seen by no row
   const Sub& b = subs[0];
   const int32_t n_keys = ra::keys_visible(d->q_len - 1, b.diag, kv_len);
-  const DecodePlan pl = decode_plan(d, n_keys);
-  const int64_t grid = (int64_t)pl.n_parts * decode_row_groups(d) * d->kv_heads * d->batch;
-  if (grid * 64 > 0xffffffffLL)   // a launch holds fewer than 2^32 work-items
-    return fail(RA_E_UNSUPPORTED, "split-KV grid of %lld waves is too large", (long long)grid);
+  const int64_t n_rg = decode_row_groups(d);
+  const ra::DecodeShape shape = ra::decode_shape(n_rg, n_keys);
+  const DecodePlan pl = decode_plan(d, shape, n_keys);
+  const int64_t waves = (int64_t)pl.n_parts * ((n_rg + shape.R - 1) / shape.R) * shape.R * shape.S *
+                        d->kv_heads * d->batch;
+  if (waves * 64 > 0xffffffffLL)   // a launch holds fewer than 2^32 work-items
+    return fail(RA_E_UNSUPPORTED, "split-KV grid of %lld waves is too large", (long long)waves);
   char* ws = static_cast<char*>(workspace);
   ra::DecodeParams p;
   p.q = st->q;
@@ -524,15 +546,13 @@ int ra_decode_step(ra_state* st, const void* k, const void* v, int32_t kv_len, i
   p.scale_log2 = d->softmax_scale * 1.4426950408889634f;
   hipStream_t stream = static_cast<hipStream_t>(d->stream);
   // the row groups of one KV head share each chunk's tiles inside one workgroup
-  const int64_t n_rg = decode_row_groups(d);
-  const int waves = n_rg >= 3 ? 4 : (int)n_rg;
-  hipError_t e = ra::launch_decode(p, d->head_dim, waves, stream);
+  hipError_t e = ra::launch_decode(p, d->head_dim, shape, stream);
   if (e != hipSuccess) return hip_fail(e, "split-KV step launch");
   ra::CombineParams c;
   c.part_o = p.part_o;
   c.part_m = p.part_m;
   c.part_l = p.part_l;
-  c.n_parts = pl.n_parts;
+  c.n_parts = pl.n_parts * shape.S;
   c.o_acc = st->o_acc;
   c.m = st->m;
   c.l = st->l;

@@ -16,6 +16,12 @@
 // are in flight while the current one is computed.  A chunk with no key, or a row that sees
 // none of a chunk's keys, gives the empty state (m = -inf, l = 0, O~ = 0), which the
 // reduction weighs by zero.  Reading K and V once is the bound: HBM.
+//
+// Several row groups per KV head (more tokens, or larger GQA groups) share each chunk inside
+// one workgroup.  Two row groups on a short block: decode_kernel with two waves sharing V
+// tiles.  Otherwise decode_ring_kernel: four waves (R row groups x S tile subsets) share a
+// five-deep LDS ring of K and V tiles, so that enough bytes stay in flight per CU with only two
+// such workgroups resident.
 
 #include <hip/hip_runtime.h>
 
@@ -36,6 +42,7 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int BK = kDecodeTileK;   // keys per tile
+constexpr int kDecodeRing = 5;     // LDS ring depth of decode_ring_kernel: 80 KB at d = 128, two workgroups per CU
 
 // s_waitcnt with vmcnt = N (six bits: [3:0] and [15:14]); expcnt and lgkmcnt not waited on
 template <int N>
@@ -295,6 +302,290 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
   }
 }
 
+// K tile [BK][D] in LDS: the score operand read (32 consecutive key rows at one chunk) hits
+// distinct banks 16 lanes at a time
+template <int D>
+__device__ __forceinline__ int k_swz(int t, int c) {
+  if constexpr (D == 128) return c ^ (t & 15);
+  else return c ^ ((t >> 1) & 7);
+}
+
+// LDS operand reads of decode_ring_kernel, issued as inline asm.  Its copies stay in flight
+// across tiles, and the compiler, which cannot follow which ring buffer they fill across the
+// loop, would otherwise wait for all of them before reading any buffer.  The asm results are
+// not ready until lgkm_wait() below, which takes them as operands so that nothing reads them
+// earlier; the explicit vmcnt waits and the barrier order the copies against these reads.
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ unsigned lds_addr(const void* p) {
+  return (unsigned)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+__device__ __forceinline__ u32x4 ds_read_b128_asm(unsigned addr) {
+  u32x4 x;
+  asm volatile("ds_read_b128 %0, %1" : "=v"(x) : "v"(addr));
+  return x;
+}
+__device__ __forceinline__ u32x2 ds_read_tr_b64_asm(unsigned addr) {
+  u32x2 x;
+  asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(x) : "v"(addr));
+  return x;
+}
+// the resident q rows, loaded ahead of the first copies so that the first tile's vmcnt wait
+// (counts complete in issue order) also covers them; pass_through() after that wait hands the
+// values on, so nothing reads them earlier
+__device__ __forceinline__ u32x4 global_load_b128_asm(const void* p) {
+  u32x4 x;
+  asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(x) : "v"(p));
+  return x;
+}
+template <int N, typename T>
+__device__ __forceinline__ void pass_through(T (&x)[N]) {
+#pragma unroll
+  for (int n = 0; n < N; ++n) asm volatile("" : "+v"(x[n]));
+}
+template <int N, typename T>
+__device__ __forceinline__ void lgkm_wait(T (&x)[N]) {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+  for (int n = 0; n < N; ++n) asm volatile("" : "+v"(x[n]));
+}
+
+// Several row groups per KV head.  A workgroup of R * S = 4 waves takes R row groups of one
+// (part, KV head); wave (r, s) computes row group r over the chunk's tiles t with t % S == s,
+// so every SIMD still holds two waves when a KV head has only two row groups (R = 2, S = 2: the
+// two tile parities are separate parts, folded by the combine).  K and V tiles both sit in an
+// NB-deep LDS ring that all four waves fill, each copying its quarter of every tile with the
+// nontemporal bit, so NB - 1 tiles are in flight per workgroup (two workgroups per CU) and each
+// tile is read from HBM once.  Per tile: wait for this wave's copies of the tile, barrier (all
+// copies landed, and every wave is done with the tile before, whose buffer is refilled next),
+// copy tile t + NB - 1, compute.
+template <int D, int R, int S, int NB>
+__global__ __launch_bounds__(64 * R * S) __attribute__((amdgpu_waves_per_eu(2))) void decode_ring_kernel(DecodeParams p) {
+  constexpr int W = R * S;
+  constexpr int KS = D / 16, VB = D / 32, RB = D * 2, CPR = D / 8, RPL = 64 / CPR;
+  constexpr int TB = BK * RB;           // bytes per tile and tensor
+  constexpr int LPT = TB / 1024;        // 1 KB copies per tile and tensor
+  static_assert(LPT % W == 0, "every wave copies the same share of a tile");
+  constexpr int LPW = LPT / W;
+  static_assert(NB >= 3 && NB <= 5, "ring depth");
+  // K at [0, TB), V at [TB, 2 TB) of each buffer; distinct objects, selected at compile time
+  __shared__ __attribute__((aligned(16))) unsigned char kv0[2 * TB];
+  __shared__ __attribute__((aligned(16))) unsigned char kv1[2 * TB];
+  __shared__ __attribute__((aligned(16))) unsigned char kv2[2 * TB];
+  __shared__ __attribute__((aligned(16))) unsigned char kv3[NB > 3 ? 2 * TB : 16];
+  __shared__ __attribute__((aligned(16))) unsigned char kv4[NB > 4 ? 2 * TB : 16];
+  auto buf = [&](auto bc) -> unsigned char* {
+    constexpr int B = decltype(bc)::value % NB;
+    if constexpr (B == 0) return kv0;
+    else if constexpr (B == 1) return kv1;
+    else if constexpr (B == 2) return kv2;
+    else if constexpr (B == 3) return kv3;
+    else return kv4;
+  };
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wr = wave % R, sub = wave / R;
+  const int r32 = lane & 31, hi = lane >> 5;
+  // grid: (part, group of R row groups, KV head, batch), part fastest
+  int L = blockIdx.x;
+  const int part = L % p.n_parts;
+  L /= p.n_parts;
+  const int n_rg = (p.group * p.n_q + 31) / 32;
+  const int n_wg = (n_rg + R - 1) / R;
+  const int rg = (L % n_wg) * R + wr;   // past the last row group: a wave with no rows
+  L /= n_wg;
+  const int g = L % p.kv_heads;
+  const int b = L / p.kv_heads;
+
+  const int pr = rg * 32 + r32;
+  const bool row_ok = pr < p.group * p.n_q;
+  const int hh = row_ok ? pr / p.n_q : 0;
+  const int i = row_ok ? pr - hh * p.n_q : 0;
+  const int h = g * p.group + hh;
+  const int64_t srow = ((int64_t)b * p.q_heads + h) * p.n_q + i;
+
+  const int k0 = part * p.chunk;
+  const int k1 = min(k0 + p.chunk, p.n_k);
+  const int n_tiles = k1 > k0 ? (k1 - k0 + BK - 1) / BK : 0;
+
+  u32x4 qf[KS];
+  {
+    const __bf16* qp = static_cast<const __bf16*>(p.q) + (int64_t)b * p.q_sb + (int64_t)h * p.q_sh + (int64_t)i * p.q_st + hi * 8;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) qf[ks] = row_ok ? global_load_b128_asm(qp + ks * 16) : u32x4{0u, 0u, 0u, 0u};
+  }
+  const float c2 = p.scale_log2;
+  float m_run = -INFINITY, l_run = 0.f;
+  f32x16 oacc[VB];
+#pragma unroll
+  for (int vb = 0; vb < VB; ++vb)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) oacc[vb][j] = 0.f;
+
+  const __bf16* kg = static_cast<const __bf16*>(p.k) + (int64_t)b * p.k_sb + (int64_t)g * p.k_sh;
+  const __bf16* vg = static_cast<const __bf16*>(p.v) + (int64_t)b * p.k_sb + (int64_t)g * p.k_sh;
+  const int row_bytes = (int)(p.k_st * 2);
+  // this wave's copies: 1 KB span wave*LPW + u of a tile holds key rows span*RPL + lane / CPR,
+  // lane at physical chunk lane % CPR (the swizzles are involutions)
+  int k_goff[LPW], v_goff[LPW];
+#pragma unroll
+  for (int u = 0; u < LPW; ++u) {
+    const int t = (wave * LPW + u) * RPL + lane / CPR;
+    k_goff[u] = (lane / CPR) * row_bytes + k_swz<D>(t, lane % CPR) * 16;
+    v_goff[u] = (lane / CPR) * row_bytes + v_swz<D>(t, lane % CPR) * 16;
+  }
+  auto copy_tile = [&](unsigned char* dst, int t0) {
+    const int64_t bytes = ((int64_t)k1 - t0) * p.k_st * 2;   // past the chunk: none, zeros land
+    const __amdgpu_buffer_rsrc_t rk = rsrc_dec(kg + (int64_t)t0 * p.k_st, bytes);
+    const __amdgpu_buffer_rsrc_t rv = rsrc_dec(vg + (int64_t)t0 * p.k_st, bytes);
+#pragma unroll
+    for (int u = 0; u < LPW; ++u) {
+      const int row0 = (wave * LPW + u) * RPL;
+      load_lds_b128_dec(rk, dst + row0 * RB, k_goff[u], row0 * row_bytes);
+      load_lds_b128_dec(rv, dst + TB + row0 * RB, v_goff[u], row0 * row_bytes);
+    }
+  };
+  int k_roff[KS];   // score operand A: key row r32, chunk 2*ks + hi
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) k_roff[ks] = r32 * RB + (k_swz<D>(r32, 2 * ks + hi) << 4);
+  int v_roff[VB];
+  {
+    const int gg = lane >> 4, a = lane & 3, e = (lane >> 2) & 3;
+    const int key = 4 * (gg >> 1) + e;
+#pragma unroll
+    for (int vb = 0; vb < VB; ++vb) {
+      const int dv = 32 * vb + 16 * (gg & 1) + 4 * a;
+      v_roff[vb] = TB + key * RB + (v_swz<D>(key, dv >> 3) << 4) + ((dv & 7) << 1);
+    }
+  }
+
+  // this wave's rows against the tile at t0 in buffer cur
+  auto compute = [&](const unsigned char* cur, int t0) {
+    const unsigned cur_a = lds_addr(cur);
+    u32x4 ka[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) ka[ks] = ds_read_b128_asm(cur_a + k_roff[ks]);
+    lgkm_wait(ka);
+    f32x16 s;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) s[j] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      bf16x8 a, bq;
+      __builtin_memcpy(&a, &ka[ks], sizeof a);
+      __builtin_memcpy(&bq, &qf[ks], sizeof bq);
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bq, s, 0, 0, 0);
+    }
+    // lane holds keys t0 + 8*(j/4) + 4*hi + (j%4) of packed row pr
+    const int lim = min(i + p.diag, k1 - 1) - t0 - 4 * hi;
+    float mx = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      s[j] = (8 * (j >> 2) + (j & 3) > lim) ? -INFINITY : s[j];
+      mx = fmaxf(mx, s[j]);
+    }
+    {
+      float a, bb;
+      pair32_dec(mx, a, bb);
+      mx = fmaxf(a, bb);
+    }
+    const float m_new = fmaxf(m_run, mx * c2);
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+    bf16x8 pk[2];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) pk[j >> 3][j & 7] = (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(s[j], c2, -m_use));
+    float rs = 0.f;
+    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      rs = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pk[kk], pk[kk], 0, 1), ones, rs, false);
+      rs = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pk[kk], pk[kk], 2, 3), ones, rs, false);
+      rs = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pk[kk], pk[kk], 4, 5), ones, rs, false);
+      rs = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pk[kk], pk[kk], 6, 7), ones, rs, false);
+    }
+    {
+      float a, bb;
+      pair32_dec(rs, a, bb);
+      rs = a + bb;
+    }
+    l_run = l_run * alpha + rs;
+    m_run = m_new;
+#pragma unroll
+    for (int vb = 0; vb < VB; ++vb)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) oacc[vb][j] *= alpha;
+    u32x2 va[2 * 2 * VB];   // (kk, vb, half)
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int vb = 0; vb < VB; ++vb) {
+        const unsigned base = cur_a + v_roff[vb] + kk * 16 * RB;
+        va[(kk * VB + vb) * 2 + 0] = ds_read_tr_b64_asm(base);
+        va[(kk * VB + vb) * 2 + 1] = ds_read_tr_b64_asm(base + 8 * RB);
+      }
+    lgkm_wait(va);
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int vb = 0; vb < VB; ++vb) {
+        const u32x4 both = __builtin_shufflevector(va[(kk * VB + vb) * 2], va[(kk * VB + vb) * 2 + 1], 0, 1, 2, 3);
+        bf16x8 a;
+        __builtin_memcpy(&a, &both, sizeof a);
+        oacc[vb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pk[kk], oacc[vb], 0, 0, 0);
+      }
+  };
+
+  // tile t in buffer B = t % NB: NB - 1 tiles are in flight on entry
+  auto step = [&](auto bc, int t) {
+    constexpr int B = decltype(bc)::value;
+    wait_vmcnt<(NB - 2) * 2 * LPW>();   // this wave's copies of tile t (and its q) have landed
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): its reads of tile t - 1 are done
+    asm volatile("s_barrier" ::: "memory");
+    pass_through(qf);
+    copy_tile(buf(std::integral_constant<int, B + NB - 1>{}), k0 + (t + NB - 1) * BK);
+    if (S == 1 || (t % S) == sub) compute(buf(bc), k0 + t * BK);
+  };
+
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  using I3 = std::integral_constant<int, 3>;
+  using I4 = std::integral_constant<int, 4>;
+  if (n_tiles > 0) {
+    copy_tile(buf(I0{}), k0);
+    copy_tile(buf(I1{}), k0 + BK);
+    if constexpr (NB > 3) copy_tile(buf(I2{}), k0 + 2 * BK);
+    if constexpr (NB > 4) copy_tile(buf(I3{}), k0 + 3 * BK);
+  }
+  // n_tiles is the same for every wave of the workgroup, so all reach the same barriers
+  for (int tt = 0; tt < n_tiles; tt += NB) {
+    step(I0{}, tt);
+    if (tt + 1 < n_tiles) step(I1{}, tt + 1);
+    if (tt + 2 < n_tiles) step(I2{}, tt + 2);
+    if constexpr (NB > 3) if (tt + 3 < n_tiles) step(I3{}, tt + 3);
+    if constexpr (NB > 4) if (tt + 4 < n_tiles) step(I4{}, tt + 4);
+  }
+  wait_vmcnt<0>();   // the copies past the chunk (zeros) land before the workgroup's LDS is freed
+
+  if (row_ok) {
+    const int64_t rows = (int64_t)p.batch * p.q_heads * p.n_q;
+    const int64_t prow = ((int64_t)part * S + sub) * rows + srow;
+    if (hi == 0) {
+      p.part_m[prow] = m_run;
+      p.part_l[prow] = l_run;
+    }
+    float* op = p.part_o + prow * D + 4 * hi;
+#pragma unroll
+    for (int vb = 0; vb < VB; ++vb)
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+        *reinterpret_cast<float4*>(op + vb * 32 + 8 * a) =
+            make_float4(oacc[vb][4 * a + 0], oacc[vb][4 * a + 1], oacc[vb][4 * a + 2], oacc[vb][4 * a + 3]);
+  }
+}
+
 // One workgroup per state row: the maximum over the parts (and the state unless fresh), then
 // l = sum_s 2^(m_s - m) l_s and O~ = sum_s 2^(m_s - m) O~_s, each thread summing one float4
 // column over a strided subset of the parts, and the subsets added through LDS.
@@ -389,23 +680,28 @@ hipError_t launch_combine(const CombineParams& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
-hipError_t launch_decode(const DecodeParams& p, int head_dim, int waves, hipStream_t stream) {
+hipError_t launch_decode(const DecodeParams& p, int head_dim, DecodeShape shape, hipStream_t stream) {
   const int n_rg = (p.group * p.n_q + 31) / 32;
-  const int n_wg = (n_rg + waves - 1) / waves;
+  const int n_wg = (n_rg + shape.R - 1) / shape.R;
   const int64_t grid = (int64_t)p.n_parts * n_wg * p.kv_heads * p.batch;
   if (grid == 0) return hipSuccess;
-#define RA_DECODE_LAUNCH(DD, WW) \
+#define RA_DECODE_ONE(DD, WW) \
   hipLaunchKernelGGL((decode_kernel<DD, WW>), dim3((unsigned)grid), dim3(64 * WW), 0, stream, p)
-  switch (head_dim * 8 + waves) {
-    case 64 * 8 + 1: RA_DECODE_LAUNCH(64, 1); break;
-    case 64 * 8 + 2: RA_DECODE_LAUNCH(64, 2); break;
-    case 64 * 8 + 4: RA_DECODE_LAUNCH(64, 4); break;
-    case 128 * 8 + 1: RA_DECODE_LAUNCH(128, 1); break;
-    case 128 * 8 + 2: RA_DECODE_LAUNCH(128, 2); break;
-    case 128 * 8 + 4: RA_DECODE_LAUNCH(128, 4); break;
+#define RA_DECODE_RING(DD, RR, SS) \
+  hipLaunchKernelGGL((decode_ring_kernel<DD, RR, SS, kDecodeRing>), dim3((unsigned)grid), dim3(64 * RR * SS), 0, stream, p)
+  switch (head_dim * 64 + shape.ring * 32 + shape.R * 4 + shape.S) {
+    case 64 * 64 + 0 + 1 * 4 + 1: RA_DECODE_ONE(64, 1); break;
+    case 64 * 64 + 0 + 2 * 4 + 1: RA_DECODE_ONE(64, 2); break;
+    case 64 * 64 + 32 + 2 * 4 + 2: RA_DECODE_RING(64, 2, 2); break;
+    case 64 * 64 + 32 + 4 * 4 + 1: RA_DECODE_RING(64, 4, 1); break;
+    case 128 * 64 + 0 + 1 * 4 + 1: RA_DECODE_ONE(128, 1); break;
+    case 128 * 64 + 0 + 2 * 4 + 1: RA_DECODE_ONE(128, 2); break;
+    case 128 * 64 + 32 + 2 * 4 + 2: RA_DECODE_RING(128, 2, 2); break;
+    case 128 * 64 + 32 + 4 * 4 + 1: RA_DECODE_RING(128, 4, 1); break;
     default: return hipErrorInvalidValue;
   }
-#undef RA_DECODE_LAUNCH
+#undef RA_DECODE_ONE
+#undef RA_DECODE_RING
   return hipGetLastError();
 }
 

@@ -131,8 +131,22 @@ hipError_t launch_step_bf16(const StepParams& p, int head_dim, hipStream_t strea
 hipError_t launch_step_f32(const StepParams& p, int head_dim, hipStream_t stream);
 hipError_t launch_finalize(const FinalizeParams& p, hipStream_t stream);
 hipError_t launch_merge(const MergeParams& p, hipStream_t stream);
-// waves: 1, 2 or 4 row groups per workgroup sharing the chunk's tiles
-hipError_t launch_decode(const DecodeParams& p, int head_dim, int waves, hipStream_t stream);
+// Workgroup shape of the split-KV step.  decode_kernel: R = 1 or 2 row groups, one wave each,
+// sharing V tiles in LDS (S = 1).  decode_ring_kernel (ring): R row groups x S tile subsets in
+// four waves that share an LDS ring of K and V tiles, each (part, subset) leaving its own
+// partial state.  Two row groups take the ring only on long blocks: below kDecodeRingMinKeys
+// visible keys more, smaller workgroups stream a short block faster than a deep ring.
+struct DecodeShape {
+  int R, S;
+  bool ring;
+};
+constexpr int64_t kDecodeRingMinKeys = 131072;
+inline DecodeShape decode_shape(int64_t row_groups, int64_t n_keys) {
+  if (row_groups <= 1) return {1, 1, false};
+  if (row_groups == 2) return n_keys < kDecodeRingMinKeys ? DecodeShape{2, 1, false} : DecodeShape{2, 2, true};
+  return {4, 1, true};
+}
+hipError_t launch_decode(const DecodeParams& p, int head_dim, DecodeShape shape, hipStream_t stream);
 hipError_t launch_combine(const CombineParams& p, hipStream_t stream);
 hipError_t launch_bwd_prep(const BwdPrepParams& p, int head_dim, bool bf16, hipStream_t stream);
 hipError_t launch_bwd_step_f32(const BwdParams& p, int head_dim, hipStream_t stream);

@@ -207,7 +207,8 @@ size_t ra_decode_workspace_bytes(const ra_desc* desc, int32_t kv_len);
  * 环流动", section 训练与推理的适用方式不同, computes decode: the few query rows are sent to many
  * shards of the keys, each shard forms a local state (m, l, O~), and a global online-softmax
  * reduction combines the local states with the running state.  Here the shards are chunks of
- * K_j/V_j, one wave of the chip each, so a block is streamed by the whole chip even when
+ * K_j/V_j, one wave of the chip each (several waves of one workgroup share a chunk when a KV
+ * head has more than 32 packed rows), so a block is streamed by the whole chip even when
  * B * Hq * q_len is far below one 128-row tile; the query heads of a GQA group are packed into
  * one wave.  Meant for short Q (decode, q_len up to a few tens); any q_len is accepted.
  * workspace: device, 256-byte aligned, at least ra_decode_workspace_bytes(desc, kv_len)

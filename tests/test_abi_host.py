@@ -342,8 +342,12 @@ def test_one_hip_runtime_per_process():
 
 
 def test_decode_workspace_bytes():
-    # chunk states: min(ceil(2048 waves / (B * Hkv * row groups of 32 packed rows)),
-    # ceil(kv_len / 256)) parts of rows * (d + 2) floats, each section 256-byte aligned
+    # chunk states of rows * (d + 2) floats, each section 256-byte aligned.  One row group of
+    # 32 packed rows per KV head: min(ceil(2048 / (B * Hkv)), ceil(kv_len / 256)) parts.
+    # Two row groups: below 131072 keys min(ceil(2048 / (B * Hkv * 2)), ceil(kv_len / 256));
+    # from there the larger of that and 2 * min(ceil(512 / (B * Hkv)), ceil(kv_len / 512)).
+    # More: R = 4 row groups per workgroup, min(ceil(512 / (B * Hkv * ceil(groups / 4))),
+    # ceil(kv_len / 256)) parts.
     lib = ra.lib()
     d = _desc(q_len=1, q_heads=64, kv_heads=8)            # 8 packed rows per KV head: one group
     rows = 64
@@ -357,11 +361,21 @@ def test_decode_workspace_bytes():
     assert lib.ra_decode_workspace_bytes(C.byref(d), 1) == expect(1)
     assert lib.ra_decode_workspace_bytes(C.byref(d), 0) == 0
     assert lib.ra_decode_workspace_bytes(C.byref(d), -1) == 0
-    d2 = _desc(q_len=5, q_heads=16, kv_heads=2)           # 40 packed rows: two groups per KV head
     a = lambda x: (x + 255) // 256 * 256                   # noqa: E731
-    parts = -(-2048 // (2 * 2))
-    assert lib.ra_decode_workspace_bytes(C.byref(d2), 1 << 20) == \
-        a(parts * 80 * 128 * 4) + 2 * a(parts * 80 * 4)
+
+    def states(parts, rows):
+        return a(parts * rows * 128 * 4) + 2 * a(parts * rows * 4)
+
+    d2 = _desc(q_len=5, q_heads=16, kv_heads=2)           # 40 packed rows: two groups per KV head
+    assert lib.ra_decode_workspace_bytes(C.byref(d2), 1 << 20) == states(512, 80)
+    assert lib.ra_decode_workspace_bytes(C.byref(d2), 600) == states(3, 80)
+    assert lib.ra_decode_workspace_bytes(C.byref(d2), 300) == states(2, 80)
+    d4 = _desc(q_len=4, q_heads=64, kv_heads=4)           # 64 packed rows, 4 KV heads
+    assert lib.ra_decode_workspace_bytes(C.byref(d4), 1 << 17) == states(max(256, 2 * 128), 64 * 4)
+    assert lib.ra_decode_workspace_bytes(C.byref(d4), 1 << 20) == states(max(256, 2 * 128), 64 * 4)
+    d3 = _desc(q_len=24, q_heads=64, kv_heads=8)          # 192 packed rows: six groups, two workgroups
+    assert lib.ra_decode_workspace_bytes(C.byref(d3), 1 << 20) == states(-(-512 // (8 * 2)), 64 * 24)
+    assert lib.ra_decode_workspace_bytes(C.byref(d3), 1000) == states(4, 64 * 24)
     bad = _desc(q_len=1, d=96)
     assert lib.ra_decode_workspace_bytes(C.byref(bad), 1000) == 0
 

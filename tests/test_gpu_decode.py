@@ -54,6 +54,9 @@ CASES = [
     (1, 16, 2, 16, 128, 3001, CONTIG, 1, 2985, 0),    # 128 packed rows: four waves share tiles
     (1, 8, 2, 20, 64, 2000, NONE, 1, 0, 0),           # 80 packed rows: three waves and an idle one
     (1, 8, 1, 20, 128, 1500, STRIPED, 4, 6003, 3),    # 160 packed rows: two four-wave workgroups
+    (2, 8, 2, 10, 64, 40000, CONTIG, 1, 39990, 0),    # two row groups at d = 64, many chunks
+    (1, 8, 1, 6, 128, 140000, CONTIG, 1, 139995, 0),  # two row groups on a long block: the ring
+    (1, 8, 1, 6, 64, 140000, CONTIG, 1, 100000, 0),   # long block, but only 100006 keys visible
 ]
 
 
@@ -182,6 +185,33 @@ def test_decode_fullsize_million_keys_sampled_heads():
         assert abs(float(lse[0, h, 0]) - float(ref_lse[0, 0, 0])) <= 2e-2
 
 
+def test_decode_fullsize_ring_sixteen_tokens():
+    """Sixteen tokens of 64 query heads over 8 KV heads (128 packed rows per KV head: four row
+    groups in one workgroup sharing an LDS ring) against 1,048,576 keys; the oracle checks
+    every row of four sampled query heads of two KV groups."""
+    import exact_long_context_amd as ra
+    B, Hq, Hkv, n, d, nk = 1, 64, 8, 16, 128, 1 << 20
+    say(f"  decode ring full size: Hq={Hq} Hkv={Hkv} tokens={n} keys={nk}")
+    vs = 1 / np.sqrt(128)
+    qd = synth.draw_device(902, synth.Q_ID, 0, B, Hq, n, d, vs, "bf16", "cuda")
+    kd = synth.draw_device(902, synth.K_ID, -1, B, Hkv, nk, d, vs, "bf16", "cuda")
+    vd = synth.draw_device(902, synth.V_ID, -1, B, Hkv, nk, d, vs, "bf16", "cuda")
+    st = ra.RingState(qd, kd)
+    st.decode_step(kd, vd, NONE)
+    o, lse = st.finalize()
+    torch.cuda.synchronize()
+    st.close()
+    kv64 = {}
+    for h in [3, 4, 56, 63]:
+        g = h // (Hq // Hkv)
+        if g not in kv64:
+            kv64.clear()
+            kv64[g] = (to64(kd[:, g:g + 1]), to64(vd[:, g:g + 1]))
+        ref, ref_lse = oracle.dense_attention(to64(qd[:, h:h + 1]), *kv64[g], np.arange(n), np.arange(nk), False)
+        assert_bf16_close(to64(o[:, h:h + 1]), ref, f"head {h} O")
+        assert np.max(np.abs(to64(lse[:, h:h + 1]) - ref_lse)) <= 2e-2
+
+
 def test_decode_is_bitwise_repeatable():
     """Three identical split-KV steps (four-wave workgroups sharing tiles, many chunks) give
     bit-identical states."""
@@ -196,6 +226,21 @@ def test_decode_is_bitwise_repeatable():
         st = ra.RingState(q, k)
         st.decode_step(k, v, NONE)
         st.decode_step(k[:, :, :1000], v[:, :, :1000], NONE)
+        torch.cuda.synchronize()
+        states.append(st.workspace.clone())
+        st.close()
+    for other in states[1:]:
+        assert torch.equal(states[0], other)
+    # the same with two row groups on a long block (four-wave workgroups on an LDS ring, two
+    # tile subsets per row group)
+    q = synth.draw_device(79, synth.Q_ID, 0, 1, 64, 8, 128, 0.3, "bf16", "cuda")
+    k = synth.draw_device(79, synth.K_ID, -1, 1, 8, 200000, 128, 0.3, "bf16", "cuda")
+    v = synth.draw_device(79, synth.V_ID, -1, 1, 8, 200000, 128, 1.0, "bf16", "cuda")
+    say("  decode repeatability: 64 heads x 8 tokens, 200000 keys")
+    states = []
+    for _ in range(3):
+        st = ra.RingState(q, k)
+        st.decode_step(k, v, NONE)
         torch.cuda.synchronize()
         states.append(st.workspace.clone())
         st.close()
