@@ -11,7 +11,7 @@
 // of 8 heads decoding one token fills 8 of the matrix instruction's 32 columns, where the
 // 128-row step tile would hold one head's single row.  Per 32-key tile: S^T = K Q^T (K rows
 // straight from HBM into registers as operand A, q resident as operand B), the online-softmax
-// update in base 2 with an exact rescale, and O~^T += V^T P^T with V staged in LDS by
+// update in base 2 (tile_update), and O~^T += V^T P^T with V staged in LDS by
 // buffer_load ... lds and read back transposed by ds_read_b64_tr_b16.  The next tile's K and V
 // are in flight while the current one is computed.  A chunk with no key, or a row that sees
 // none of a chunk's keys, gives the empty state (m = -inf, l = 0, O~ = 0), which the
@@ -77,6 +77,63 @@ __device__ __forceinline__ void pair32_dec(float x, float& a, float& b) {
   b = __uint_as_float(r[1]);
 }
 
+// The online-softmax update of one 32-key tile for a wave's 32 packed rows, in base 2.  s holds
+// S^T (lane: keys 8*(j/4) + 4*hi + (j%4) of its row, masked here past lim); visible says the
+// row sees some key of the tile.  The reference m of a row may lag its true maximum: the tile's
+// terms 2^(x - m) are taken as they come while their row sum stays <= 2^32, which fp32 and bf16
+// hold without loss; only a row past that, or one meeting its first visible key, takes the
+// tile's maximum and rescales l and O~, so that max x - 32 <= m <= max x holds throughout.
+// Before any key m = 0 and l = 0.  The probabilities come back in bf16 (operand B of the value
+// product), and the row sum adds the same rounded values.
+constexpr float kDecodeSumMax = 4294967296.0f;   // 2^32
+
+template <int VB>
+__device__ __forceinline__ void tile_update(f32x16& s, int lim, bool visible, float c2, float& m_run,
+                                            float& l_run, f32x16 (&oacc)[VB], bf16x8 (&pk)[2]) {
+#pragma unroll
+  for (int j = 0; j < 16; ++j) s[j] = (8 * (j >> 2) + (j & 3) > lim) ? -INFINITY : s[j];
+  auto probs = [&](float ref) {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) pk[j >> 3][j & 7] = (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(s[j], c2, -ref));
+    float r = 0.f;
+    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      r = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pk[kk], pk[kk], 0, 1), ones, r, false);
+      r = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pk[kk], pk[kk], 2, 3), ones, r, false);
+      r = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pk[kk], pk[kk], 4, 5), ones, r, false);
+      r = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pk[kk], pk[kk], 6, 7), ones, r, false);
+    }
+    float a, b;
+    pair32_dec(r, a, b);
+    return a + b;
+  };
+  float rs = probs(m_run);
+  const bool bad = !(rs <= kDecodeSumMax) || (l_run == 0.f && visible);
+  if (__builtin_amdgcn_ballot_w64(bad)) {
+    float mx = s[0];
+#pragma unroll
+    for (int j = 1; j < 16; ++j) mx = fmaxf(mx, s[j]);
+    {
+      float a, b;
+      pair32_dec(mx, a, b);
+      mx = fmaxf(a, b);
+    }
+    // a bad row moves its reference to the tile's maximum: l and O~ scale by 2^-shift (a row
+    // that has seen nothing holds zeros and takes 0: 2^-shift may overflow there)
+    const float shift = (bad && mx != -INFINITY) ? mx * c2 - m_run : 0.f;
+    const float alpha = l_run == 0.f ? 0.f : __builtin_amdgcn_exp2f(-shift);
+    l_run *= alpha;
+#pragma unroll
+    for (int vb = 0; vb < VB; ++vb)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) oacc[vb][j] *= alpha;
+    m_run += shift;
+    rs = probs(m_run);
+  }
+  l_run += rs;
+}
+
 // W waves per workgroup: the W row groups of one (part, KV head) share the chunk's V tiles in
 // LDS, each wave loading 1/W of every tile; their K loads are the same addresses at nearly the
 // same time, served once from HBM.  With one wave, two V buffers and no barrier; with several,
@@ -135,7 +192,7 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
     }
   }
   const float c2 = p.scale_log2;
-  float m_run = -INFINITY, l_run = 0.f;
+  float m_run = 0.f, l_run = 0.f;   // m: the finite reference of l and O~ (0 before any key)
   f32x16 oacc[VB];
 #pragma unroll
   for (int vb = 0; vb < VB; ++vb)
@@ -197,50 +254,21 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
     } else {
       __builtin_amdgcn_wave_barrier();
     }
-    f32x16 s;
+    // two independent accumulation chains over the contraction, added at the end
+    f32x16 s, s1;
 #pragma unroll
-    for (int j = 0; j < 16; ++j) s[j] = 0.f;
+    for (int j = 0; j < 16; ++j) s[j] = s1[j] = 0.f;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kc[ks], qf[ks], s, 0, 0, 0);
+    for (int ks = 0; ks < KS; ks += 2) {
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kc[ks], qf[ks], s, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kc[ks + 1], qf[ks + 1], s1, 0, 0, 0);
+    }
+#pragma unroll
+    for (int j = 0; j < 16; ++j) s[j] += s1[j];
     // lane holds keys t0 + 8*(j/4) + 4*hi + (j%4) of packed row pr
     const int lim = min(i + p.diag, k1 - 1) - t0 - 4 * hi;
-    float mx = -INFINITY;
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      s[j] = (8 * (j >> 2) + (j & 3) > lim) ? -INFINITY : s[j];
-      mx = fmaxf(mx, s[j]);
-    }
-    {
-      float a, bb;
-      pair32_dec(mx, a, bb);
-      mx = fmaxf(a, bb);
-    }
-    const float m_new = fmaxf(m_run, mx * c2);
-    const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
     bf16x8 pk[2];
-#pragma unroll
-    for (int j = 0; j < 16; ++j) pk[j >> 3][j & 7] = (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(s[j], c2, -m_use));
-    float rs = 0.f;
-    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      rs = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pk[kk], pk[kk], 0, 1), ones, rs, false);
-      rs = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pk[kk], pk[kk], 2, 3), ones, rs, false);
-      rs = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pk[kk], pk[kk], 4, 5), ones, rs, false);
-      rs = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pk[kk], pk[kk], 6, 7), ones, rs, false);
-    }
-    {
-      float a, bb;
-      pair32_dec(rs, a, bb);
-      rs = a + bb;
-    }
-    l_run = l_run * alpha + rs;
-    m_run = m_new;
-#pragma unroll
-    for (int vb = 0; vb < VB; ++vb)
-#pragma unroll
-      for (int j = 0; j < 16; ++j) oacc[vb][j] *= alpha;
+    tile_update(s, lim, lim + 4 * hi >= 0, c2, m_run, l_run, oacc, pk);
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
@@ -289,7 +317,7 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
     const int64_t rows = (int64_t)p.batch * p.q_heads * p.n_q;
     const int64_t prow = (int64_t)part * rows + srow;
     if (hi == 0) {
-      p.part_m[prow] = m_run;
+      p.part_m[prow] = l_run == 0.f ? -INFINITY : m_run;
       p.part_l[prow] = l_run;
     }
     float* op = p.part_o + prow * D + 4 * hi;
@@ -416,7 +444,7 @@ __global__ __launch_bounds__(64 * R * S) __attribute__((amdgpu_waves_per_eu(2)))
     for (int ks = 0; ks < KS; ++ks) qf[ks] = row_ok ? global_load_b128_asm(qp + ks * 16) : u32x4{0u, 0u, 0u, 0u};
   }
   const float c2 = p.scale_log2;
-  float m_run = -INFINITY, l_run = 0.f;
+  float m_run = 0.f, l_run = 0.f;   // m: the finite reference of l and O~ (0 before any key)
   f32x16 oacc[VB];
 #pragma unroll
   for (int vb = 0; vb < VB; ++vb)
@@ -467,55 +495,25 @@ __global__ __launch_bounds__(64 * R * S) __attribute__((amdgpu_waves_per_eu(2)))
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) ka[ks] = ds_read_b128_asm(cur_a + k_roff[ks]);
     lgkm_wait(ka);
-    f32x16 s;
+    f32x16 s, s1;   // two independent accumulation chains, added at the end
 #pragma unroll
-    for (int j = 0; j < 16; ++j) s[j] = 0.f;
+    for (int j = 0; j < 16; ++j) s[j] = s1[j] = 0.f;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      bf16x8 a, bq;
-      __builtin_memcpy(&a, &ka[ks], sizeof a);
-      __builtin_memcpy(&bq, &qf[ks], sizeof bq);
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bq, s, 0, 0, 0);
+    for (int ks = 0; ks < KS; ks += 2) {
+      bf16x8 a0, b0, a1, b1;
+      __builtin_memcpy(&a0, &ka[ks], sizeof a0);
+      __builtin_memcpy(&b0, &qf[ks], sizeof b0);
+      __builtin_memcpy(&a1, &ka[ks + 1], sizeof a1);
+      __builtin_memcpy(&b1, &qf[ks + 1], sizeof b1);
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b0, s, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b1, s1, 0, 0, 0);
     }
+#pragma unroll
+    for (int j = 0; j < 16; ++j) s[j] += s1[j];
     // lane holds keys t0 + 8*(j/4) + 4*hi + (j%4) of packed row pr
     const int lim = min(i + p.diag, k1 - 1) - t0 - 4 * hi;
-    float mx = -INFINITY;
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      s[j] = (8 * (j >> 2) + (j & 3) > lim) ? -INFINITY : s[j];
-      mx = fmaxf(mx, s[j]);
-    }
-    {
-      float a, bb;
-      pair32_dec(mx, a, bb);
-      mx = fmaxf(a, bb);
-    }
-    const float m_new = fmaxf(m_run, mx * c2);
-    const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
     bf16x8 pk[2];
-#pragma unroll
-    for (int j = 0; j < 16; ++j) pk[j >> 3][j & 7] = (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(s[j], c2, -m_use));
-    float rs = 0.f;
-    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      rs = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pk[kk], pk[kk], 0, 1), ones, rs, false);
-      rs = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pk[kk], pk[kk], 2, 3), ones, rs, false);
-      rs = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pk[kk], pk[kk], 4, 5), ones, rs, false);
-      rs = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pk[kk], pk[kk], 6, 7), ones, rs, false);
-    }
-    {
-      float a, bb;
-      pair32_dec(rs, a, bb);
-      rs = a + bb;
-    }
-    l_run = l_run * alpha + rs;
-    m_run = m_new;
-#pragma unroll
-    for (int vb = 0; vb < VB; ++vb)
-#pragma unroll
-      for (int j = 0; j < 16; ++j) oacc[vb][j] *= alpha;
+    tile_update(s, lim, lim + 4 * hi >= 0, c2, m_run, l_run, oacc, pk);
     u32x2 va[2 * 2 * VB];   // (kk, vb, half)
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk)
@@ -573,7 +571,7 @@ __global__ __launch_bounds__(64 * R * S) __attribute__((amdgpu_waves_per_eu(2)))
     const int64_t rows = (int64_t)p.batch * p.q_heads * p.n_q;
     const int64_t prow = ((int64_t)part * S + sub) * rows + srow;
     if (hi == 0) {
-      p.part_m[prow] = m_run;
+      p.part_m[prow] = l_run == 0.f ? -INFINITY : m_run;
       p.part_l[prow] = l_run;
     }
     float* op = p.part_o + prow * D + 4 * hi;
