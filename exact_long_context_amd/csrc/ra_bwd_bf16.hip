@@ -201,48 +201,36 @@ void bwd_dq_kernel(BwdParams p) {
     map.load(v_tiles[1 - B], vg, (int64_t)(kt + 1) * BT, p.n_k, p.k_st, wave, row_bytes);
     const unsigned char* kt_b = k_tiles[B];
     const unsigned char* vt_b = v_tiles[B];
-    f32x16 s[NH], dp[NH];
+    // the element mask only on tiles that cross the diagonal or the block's end for some row of
+    // the wave
+    const bool full = (kt + 1) * BT - 1 <= i0 + wave * WR + p.diag && (kt + 1) * BT <= p.n_k;
+    const int lim = min(row + p.diag, p.n_k - 1) - kt * BT - 4 * hi;
+    // one 32-key half at a time (scores, dP, dS, then its share of dQ): with both halves' scores
+    // live at once this kernel spilled at d = 128
 #pragma unroll
-    for (int kh = 0; kh < NH; ++kh)
+    for (int kh = 0; kh < NH; ++kh) {
+      f32x16 s, dp;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) s[j] = dp[j] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(map.rd(kt_b, ks, kh), qf[ks], s, 0, 0, 0);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(map.rd(vt_b, ks, kh), dof[ks], dp, 0, 0, 0);
+      }
+      // lane holds keys 32*kh + 8*(j/4) + 4*hi + (j%4) of this row
+      bf16x8 dsk[2];
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
-        s[kh][j] = 0.f;
-        dp[kh][j] = 0.f;
+        const bool ok = full || 32 * kh + 8 * (j >> 2) + (j & 3) <= lim;
+        const float pr = ok ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[j], c2, -lse2)) : 0.f;
+        dsk[j >> 3][j & 7] = (__bf16)(pr * (dp[j] - Dr) * p.scale);
       }
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
+      for (int k2 = 0; k2 < 2; ++k2)
 #pragma unroll
-      for (int kh = 0; kh < NH; ++kh) {
-        s[kh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(map.rd(kt_b, ks, kh), qf[ks], s[kh], 0, 0, 0);
-        dp[kh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(map.rd(vt_b, ks, kh), dof[ks], dp[kh], 0, 0, 0);
-      }
-    // lane holds keys 32*kh + 8*(j/4) + 4*hi + (j%4) of this row; the element mask only on
-    // tiles that cross the diagonal or the block's end for some row of the wave
-    bf16x8 dsk[2 * NH];
-    if ((kt + 1) * BT - 1 <= i0 + wave * WR + p.diag && (kt + 1) * BT <= p.n_k) {
-#pragma unroll
-      for (int kh = 0; kh < NH; ++kh)
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kh][j], c2, -lse2));
-          dsk[2 * kh + (j >> 3)][j & 7] = (__bf16)(pr * (dp[kh][j] - Dr) * p.scale);
-        }
-    } else {
-      const int lim = min(row + p.diag, p.n_k - 1) - kt * BT - 4 * hi;
-#pragma unroll
-      for (int kh = 0; kh < NH; ++kh)
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          const bool ok = 32 * kh + 8 * (j >> 2) + (j & 3) <= lim;
-          const float pr = ok ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[kh][j], c2, -lse2)) : 0.f;
-          dsk[2 * kh + (j >> 3)][j & 7] = (__bf16)(pr * (dp[kh][j] - Dr) * p.scale);
-        }
+        for (int vb = 0; vb < VB; ++vb)
+          dq[vb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(map.rd_t(kt_b, 2 * kh + k2, vb), dsk[k2], dq[vb], 0, 0, 0);
     }
-#pragma unroll
-    for (int kk = 0; kk < 2 * NH; ++kk)
-#pragma unroll
-      for (int vb = 0; vb < VB; ++vb)
-        dq[vb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(map.rd_t(kt_b, kk, vb), dsk[kk], dq[vb], 0, 0, 0);
     __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's copies of the next tile
     __syncthreads();
   };
