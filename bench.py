@@ -5,7 +5,7 @@ A step is one whole lap: the empty state, P block steps (each block after the
 rank's own arrives through an emulated ring transfer on a side stream), and the
 finalize pass, on seeded synthetic bf16 inputs already resident in HBM.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--rank R]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--rank R] [--lap-only]
 
 Prints ONE JSON line.  ``value`` is useful attention TFLOP/s: 4 * head_dim flops
 per allowed (query, key) pair per query head, over the timed laps.  The
@@ -13,6 +13,11 @@ per allowed (query, key) pair per query head, over the timed laps.  The
 average launch time, from HIP events recorded around each launch on the compute
 stream) against the MI355X dense bf16 MFMA peak; ``cpu_baseline`` times the
 fp64 oracle on this host's cores over a bounded sample of the same workload.
+
+On a bf16 workload the line's ``detail`` also holds, unless ``--lap-only`` (or only some of
+them are named by flag): the HBM-bound passes (finalize, short KV blocks, the merge of shard
+states), the backward lap, and the split-KV decode step, the last two each with the oracle
+timed beside it.
 """
 
 from __future__ import annotations
@@ -316,12 +321,14 @@ def main() -> int:
     ap.add_argument("--rank", type=int, default=None, help="measured rank (default: the workload's first)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="oracle timing budget")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--lap-only", action="store_true",
+                    help="time the forward lap only: none of the passes below")
     ap.add_argument("--backward", action="store_true",
-                    help="also time the backward lap (ra_bwd_*) after the forward laps")
+                    help="time the backward lap (ra_bwd_*) after the forward laps")
     ap.add_argument("--decode", action="store_true",
-                    help="also time the split-KV step for few query rows (decode) against 16K..1M keys")
+                    help="time the split-KV step for few query rows (decode) against 16K..1M keys")
     ap.add_argument("--hbm-passes", action="store_true",
-                    help="also time the HBM-bound passes (finalize, short KV blocks, state merge)")
+                    help="time the HBM-bound passes (finalize, short KV blocks, state merge)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -417,11 +424,21 @@ def main() -> int:
         "avg_launch_ms": round(avg_kernel_ms, 4),
     }
 
-    hbm = hbm_passes(ra, qd, kb[0], vb[0], ws, w, desc) if args.hbm_passes else None
+    # the passes beside the lap: those named by flag, else all of them on a bf16 workload
+    # (none with --lap-only)
+    named = args.backward or args.decode or args.hbm_passes
+    every = not args.lap_only and not named and w.dtype == "bf16"
+    hbm = bwd = dec = None
     side_cpu = 0.0 if args.no_cpu_baseline else 5.0
-    bwd = backward_lap(ra, qd, kb, vb, out, lse, w, rank, mask, order, step_flops, args.steps, side_cpu) \
-        if args.backward else None
-    dec = decode_passes(ra, cpu_seconds=side_cpu) if args.decode else None
+    if args.hbm_passes or every:
+        log("[bench] HBM-bound passes: finalize, short KV blocks, state merge")
+        hbm = hbm_passes(ra, qd, kb[0], vb[0], ws, w, desc)
+    if args.backward or every:
+        log("[bench] backward lap")
+        bwd = backward_lap(ra, qd, kb, vb, out, lse, w, rank, mask, order, step_flops, args.steps, side_cpu)
+    if args.decode or every:
+        log("[bench] split-KV decode steps")
+        dec = decode_passes(ra, cpu_seconds=side_cpu)
 
     cpu = None
     if not args.no_cpu_baseline:
