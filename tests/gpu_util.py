@@ -27,7 +27,7 @@ def say(msg: str) -> None:
 
 
 def require_gpu():
-    assert torch.cuda.is_available(), "GPU tests need an MI355X; run them with -m gpu on the GPU box"
+    assert torch.cuda.is_available(), "GPU tests need an MI355X: run them with -m gpu on a machine that has one"
     import exact_long_context_amd  # noqa: F401  (fails loudly if librocring.so is missing)
 
 
