@@ -8,7 +8,9 @@
 // buffer it already owns).  Events carry the two hazards the double-buffer scheme must
 // respect ("Ring Attention：把超长序列沿设备环流动", section 双缓冲是重叠成立的基础): a receive
 // buffer is not overwritten before the kernel that reads it has finished (ev_free), and
-// the kernel does not read a buffer before its transfer has landed (ev_ready).
+// the kernel does not read a buffer before its transfer has landed (ev_ready).  A block that
+// no query of the rank sees (a causal block wholly in the future) launches no kernel: its
+// buffer is free once it has landed, and the next transfer into it waits for nothing else.
 //
 // Block visit order: at step s rank r holds block (r - s) mod P, the order of the
 // four-device table on the same page (section 环是怎样工作的).
@@ -90,12 +92,35 @@ extern "C" int ra_ring_lap_emulated(const ra_desc* desc, const void* q, void* wo
 
   const int r = lap->rank;
   const bool copies = lap->kv_len > 0 && P > 1;
+  // positions of step s's block, and whether any query of this rank sees a key of it
+  auto offsets = [&](int j, int64_t* q_off, int64_t* k_off) {
+    *q_off = 0;
+    *k_off = 0;
+    if (lap->mask_kind == RA_MASK_CAUSAL_CONTIGUOUS) {
+      *q_off = (int64_t)r * desc->q_len;
+      *k_off = (int64_t)j * lap->kv_len;
+    } else if (lap->mask_kind == RA_MASK_CAUSAL_STRIPED || lap->mask_kind == RA_MASK_CAUSAL_ZIGZAG) {
+      *q_off = r;
+      *k_off = j;
+    }
+  };
+  auto keys_of = [&](int j) { return lap->kv_valid ? lap->kv_valid[j] : lap->kv_len; };
+  auto runs = [&](int s) {
+    const int j = ((r - s) % P + P) % P;
+    int64_t qo, ko;
+    offsets(j, &qo, &ko);
+    ra_stats st;
+    return ra_plan_block(desc, keys_of(j), lap->mask_kind, qo, ko, &st) != RA_OK || st.blocks_run > 0;
+  };
   for (int s = 0; s < P; ++s) {
     const int j = ((r - s) % P + P) % P;
     if (copies && s + 1 < P) {  // post the receive of the next block
       const int nb = (s + 1) & 1;
       const int jn = ((r - s - 1) % P + P) % P;
-      if (s + 1 >= 3 && (e = hipStreamWaitEvent(ss, ev.freed[nb], 0)) != hipSuccess)
+      // the buffer's previous block (step s - 1) must have been read by its kernel; a block
+      // that no query sees launches nothing and frees its buffer as soon as it has landed,
+      // which the side stream's own order already gives
+      if (s + 1 >= 3 && runs(s - 1) && (e = hipStreamWaitEvent(ss, ev.freed[nb], 0)) != hipSuccess)
         return ra::set_hip_error(e, "stream wait");
       if (lap->poison) {
         if ((e = hipMemsetAsync(lap->recv_k[nb], 0xFF, lap->block_bytes, ss)) != hipSuccess ||
@@ -117,19 +142,13 @@ extern "C" int ra_ring_lap_emulated(const ra_desc* desc, const void* q, void* wo
       kp = lap->recv_k[s & 1];
       vp = lap->recv_v[s & 1];
     }
-    int64_t q_off = 0, k_off = 0;
-    if (lap->mask_kind == RA_MASK_CAUSAL_CONTIGUOUS) {
-      q_off = (int64_t)r * desc->q_len;
-      k_off = (int64_t)j * lap->kv_len;
-    } else if (lap->mask_kind == RA_MASK_CAUSAL_STRIPED || lap->mask_kind == RA_MASK_CAUSAL_ZIGZAG) {
-      q_off = r;
-      k_off = j;
-    }
+    int64_t q_off, k_off;
+    offsets(j, &q_off, &k_off);
     if (lap->step_events &&
         (e = hipEventRecord(static_cast<hipEvent_t>(lap->step_events[2 * s]), cs)) != hipSuccess)
       return ra::set_hip_error(e, "event record");
     // padding past a block's real keys is cut off by the key count: no query sees it
-    const int32_t keys = lap->kv_valid ? lap->kv_valid[j] : lap->kv_len;
+    const int32_t keys = keys_of(j);
     rc = ra_block_step(g.st, kp, vp, keys, lap->mask_kind, q_off, k_off);
     if (rc) return rc;
     if (lap->step_events &&

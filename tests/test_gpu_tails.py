@@ -58,6 +58,7 @@ CASES = [
     ("f32", 2, 1, 128, 777, 8, CONTIG),       # capacity 98, last rank 91
     ("f32", 2, 1, 64, 777, 8, STRIPED),
     ("bf16", 2, 1, 128, 49, 8, CONTIG),       # capacity 7: the last rank holds no token
+    ("bf16", 2, 1, 128, 49, 8, NONE),         # the empty block 7 mid-lap, live blocks after it
 ]
 
 
