@@ -165,6 +165,50 @@ def test_backward_full_size_sampled_rows_and_keys():
     assert_bf16_close(to64(dv0[:, :1, keys]), gv, "dV sampled keys", rowwise=None)
 
 
+def test_backward_full_size_noncausal_lap_sampled():
+    """The backward lap that bench.py times: the non-causal 131072-token, 8-rank ring, rank 0,
+    32 heads, all 8 blocks through ra_bwd_block_step in ring order.  Sampled dQ rows of head 0
+    against every key of the sequence, and sampled keys of one travelling block's dK and dV
+    (this rank's contribution: every one of its rows), against the oracle, whose forward for
+    head 0 (O, lse over all keys) it computes itself."""
+    import exact_long_context_amd as ra
+    from exact_long_context_amd.workload import shard_blocks
+    from gpu_util import seeded_rows
+    w = synth.WORKLOADS["noncausal_n131072_p8_h32"]
+    rank, j_check = 0, 3
+    say(f"  generating {w.name} rank {rank}")
+    q, k, v = synth.workload_tensors(w, rank)
+    n = w.n_local
+    d_out = synth.random_case(10, 1, w.q_heads, 1, n, 1, w.head_dim, "bf16")[0]
+    kb, vb = shard_blocks(k.cuda(), v.cuda(), w.P, w.layout)
+    qd, dod = q.cuda(), d_out.cuda()
+    o, lse, _ = ra.EmulatedRing(kb, vb).lap(qd, rank, NONE)
+    bw = ra.RingBackward(qd, dod, o, lse, kb[0], ring_size=w.P)
+    dks = {j: torch.zeros(kb[j].shape, dtype=torch.float32, device="cuda") for j in range(w.P)}
+    dvs = {j: torch.zeros(kb[j].shape, dtype=torch.float32, device="cuda") for j in range(w.P)}
+    for j in oracle.ring_visit_order(w.P, rank):
+        bw.step(kb[j], vb[j], dks[j], dvs[j], NONE, 0, 0)
+    dq = bw.finalize()
+    bw.close()
+    torch.cuda.synchronize()
+    # oracle, head 0: the rank's rows against the whole sequence
+    q64, k64, v64, do64 = to64(q[:, :1]), to64(k[:, :1]), to64(v[:, :1]), to64(d_out[:, :1])
+    q_pos, k_pos = np.arange(n), np.arange(w.N)
+    say("  oracle forward, head 0, all keys")
+    o_ref, lse_ref = oracle.dense_attention(q64, k64, v64, q_pos, k_pos, False, row_chunk=512)
+    D = oracle.backward_row_terms(do64, o_ref)
+    rows = seeded_rows(n, 48, 5)
+    gq, _, _ = oracle.backward_block(q64[:, :, rows], k64, v64, do64[:, :, rows], lse_ref[:, :, rows],
+                                     D[:, :, rows], q_pos[rows], k_pos, False)
+    assert_bf16_close(to64(dq[:, :1, rows]), gq, "dQ sampled rows, all keys", rowwise=None)
+    keys = seeded_rows(n, 48, 6)                       # local keys of block j_check
+    gk_keys = j_check * n + keys                       # their global positions
+    _, gk, gv = oracle.backward_block(q64, k64[:, :, gk_keys], v64[:, :, gk_keys], do64, lse_ref, D,
+                                      q_pos, gk_keys, False)
+    assert_bf16_close(to64(dks[j_check][:, :1, keys]), gk, f"dK block {j_check} sampled keys", rowwise=None)
+    assert_bf16_close(to64(dvs[j_check][:, :1, keys]), gv, f"dV block {j_check} sampled keys", rowwise=None)
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_backward_is_bitwise_repeatable(dtype):
     """Three identical backward steps over 4096 rows x 8 heads (many workgroups on every CU):
