@@ -58,6 +58,7 @@ CASES = [
     (1, 8, 1, 6, 128, 140000, CONTIG, 1, 139995, 0),  # two row groups on a long block: the ring
     (1, 8, 1, 6, 64, 140000, CONTIG, 1, 100000, 0),   # long block, but only 100006 keys visible
     (1, 8, 1, 6, 64, 133000, NONE, 1, 0, 0),          # two row groups, ring at d = 64
+    (2, 8, 1, 12, 128, 5000, STRIPED, 4, 19997, 2),   # batch 2, three row groups on the ring
 ]
 
 
