@@ -93,6 +93,12 @@ int check_desc(const ra_desc* d) {
   }
   if (d->q_len > 1 && d->q_strides[2] < d->head_dim)
     return fail(RA_E_INVALID, "q token stride smaller than head_dim");
+  // every launch over the query rows (64-row tiles at the smallest, 256 threads each) must
+  // hold fewer than 2^32 work-items
+  const int64_t q_tiles = ((int64_t)d->q_len + 63) / 64;
+  if (q_tiles * d->q_heads * d->batch * 256 > 0xffffffffLL)
+    return fail(RA_E_UNSUPPORTED, "%lld query tiles of 64 rows exceed one launch",
+                (long long)(q_tiles * d->q_heads * d->batch));
   return RA_OK;
 }
 
@@ -639,6 +645,10 @@ int ra_bwd_block_step(ra_bwd* st, const void* k, const void* v, float* dk, float
       return fail(RA_E_INVALID, "K_j, V_j, dK_j and dV_j must be 16-byte aligned");
     if (kv_len > 1 && d->kv_strides[2] < d->head_dim)
       return fail(RA_E_INVALID, "kv token stride smaller than head_dim");
+    // the key-stationary launches: 32-key tiles at the smallest, 256 threads each
+    const int64_t k_tiles = ((int64_t)kv_len + 31) / 32;
+    if (k_tiles * d->kv_heads * d->batch * 256 > 0xffffffffLL)
+      return fail(RA_E_UNSUPPORTED, "%lld key tiles exceed one launch", (long long)(k_tiles * d->kv_heads * d->batch));
   }
   s.tile_q = st->stats.tile_q;
   s.tile_k = st->stats.tile_k;

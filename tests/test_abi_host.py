@@ -241,6 +241,12 @@ def test_invalid_descriptors():
     assert _init(_desc(), q=0x10008)[0] == ra.RA_E_INVALID       # misaligned Q
     assert _init(_desc(), ws=0x20010)[0] == ra.RA_E_INVALID      # workspace not 256-aligned
     assert b"multiple" in lib.ra_status_string(ra.RA_E_INVALID) or True
+    # more query tiles than one launch can hold (2^30 rows x 16 heads: 2^28 tiles of 64 rows)
+    big = _desc(q_len=1 << 30, q_heads=16, kv_heads=16)
+    assert _init(big)[0] == ra.RA_E_UNSUPPORTED
+    assert lib.ra_workspace_bytes(C.byref(big)) == 0
+    ok = _desc(q_len=1 << 20, q_heads=64, kv_heads=8)      # 2^20 tiles x 256 threads: fits
+    assert lib.ra_workspace_bytes(C.byref(ok)) > 0
 
 
 def test_workspace_layout():
