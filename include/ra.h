@@ -66,7 +66,8 @@ extern "C" {
 /* ---- status codes ---------------------------------------------------------------- */
 #define RA_OK 0
 #define RA_E_INVALID (-1)     /* null pointer, bad dimension, q_heads % kv_heads != 0, bad stride or alignment */
-#define RA_E_UNSUPPORTED (-2) /* head_dim or dtype without a compiled kernel, or a form a call does not take */
+#define RA_E_UNSUPPORTED (-2) /* head_dim or dtype without a compiled kernel, a form a call does not
+                                 take, or more tiles than one launch holds (2^32 work-items) */
 #define RA_E_STATE (-3)       /* step or finalize on a finalized state, double finalize */
 #define RA_E_HIP (-4)         /* a HIP runtime call or kernel launch failed */
 
