@@ -99,6 +99,7 @@ def cpu_baseline(w, rank: int, q, k, v, seconds: float):
         "value": flops / el / 1e12,
         "unit": "TFLOP/s",
         "cores": int(threads),
+        "blas": host_blas(),
         "kind": "oracle",
         "sample": (f"fp64 dense attention (oracle.dense_attention) of head 0, local rows 0..{done_rows - 1} "
                    f"of rank {rank} against all {w.N} keys, {el:.1f} s; same useful-flop accounting"),
@@ -112,6 +113,17 @@ def host_threads() -> int:
         return max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     except Exception:
         return len(os.sched_getaffinity(0))
+
+
+def host_blas() -> str:
+    """The BLAS library NumPy's fp64 products run on, as threadpoolctl names it."""
+    try:
+        from threadpoolctl import threadpool_info
+        libs = [f"{i.get('internal_api', '?')} {i.get('version', '')}".strip()
+                for i in threadpool_info() if i.get("user_api") == "blas"]
+        return ", ".join(libs) if libs else "unknown"
+    except Exception:
+        return "unknown"
 
 
 def cpu_backward_baseline(w, rank: int, j: int, q, kb, vb, d_out, seconds: float):
@@ -139,7 +151,7 @@ def cpu_backward_baseline(w, rank: int, j: int, q, kb, vb, d_out, seconds: float
         flops += 10 * w.head_dim * oracle.live_pair_count(q_pos[rows], k_pos, causal)
         done += rows.size
     return {"value": round(flops / timed / 1e12, 5) if timed > 0 else 0.0, "unit": "TFLOP/s",
-            "cores": host_threads(), "kind": "oracle",
+            "cores": host_threads(), "blas": host_blas(), "kind": "oracle",
             "sample": (f"fp64 oracle.backward_block of query head 0, local rows 0..{done - 1} of rank {rank} "
                        f"against the {k_pos.size} keys of block {j}, {timed:.1f} s timed; 10*d flops per allowed pair"),
             "seconds": round(timed, 3)}
@@ -166,7 +178,7 @@ def cpu_decode_baseline(seconds: float):
     el = time.perf_counter() - t0
     kv_bytes = 2 * B * Hkv * nk * d * 2
     return {"value": round(kv_bytes * calls / el / 1e9, 3), "unit": "GB/s",
-            "cores": host_threads(), "kind": "oracle",
+            "cores": host_threads(), "blas": host_blas(), "kind": "oracle",
             "sample": (f"fp64 oracle.online_block_update, 1 token x 64 query heads over 8 KV heads against "
                        f"{nk} keys, {calls} calls in {el:.1f} s; K+V bytes as bf16"),
             "seconds": round(el, 3)}
