@@ -184,7 +184,45 @@ def cpu_decode_baseline(seconds: float):
             "seconds": round(el, 3)}
 
 
-def hbm_passes(ra, q, k, v, ws, w, desc, reps: int = 20):
+def cpu_hbm_baselines(d: int, seconds: float):
+    """The oracle's finalize, merge of 8 shard states and short-block update on this host:
+    one head of 16384 query rows, fp64, each repeated for about `seconds`; reported in the
+    same algorithmic bytes per second as the GPU passes (fp32 state, bf16 K/V)."""
+    import numpy as np
+    import oracle
+    rng = np.random.default_rng(3)
+    n = 16384
+
+    def state():
+        return {"m": rng.standard_normal((1, 1, n)), "l": rng.random((1, 1, n)) + 1.0,
+                "o": rng.standard_normal((1, 1, n, d))}
+
+    def rate(fn, nbytes):
+        calls, t0 = 0, time.perf_counter()
+        while calls == 0 or time.perf_counter() - t0 < seconds:
+            fn()
+            calls += 1
+        el = time.perf_counter() - t0
+        return {"value": round(nbytes * calls / el / 1e9, 3), "unit": "GB/s", "calls": calls,
+                "seconds": round(el, 3)}
+
+    res = {}
+    st = state()
+    res["finalize"] = rate(lambda: oracle.online_finalize(st), n * (4 * d + 8) + n * (4 * d + 4))
+    parts = [state() for _ in range(8)]
+    res["merge_8_parts"] = rate(lambda: oracle.merge_states(parts), 8 * n * (4 * d + 8) + n * (4 * d + 4))
+    q = rng.standard_normal((1, 1, n, d))
+    for nk in (256, 1024):
+        kk, vv = rng.standard_normal((1, 1, nk, d)), rng.standard_normal((1, 1, nk, d))
+        nbytes = 2 * n * (4 * d + 8) + n * d * 2 + 2 * nk * d * 2
+        res[f"step_nk{nk}"] = rate(lambda: oracle.online_block_update(st, q, kk, vv, np.arange(n),
+                                                                      np.arange(nk), False), nbytes)
+    return {"kind": "oracle", "cores": host_threads(), "blas": host_blas(),
+            "sample": "fp64 oracle online_finalize, merge_states of 8 parts and online_block_update "
+                      "(Nk 256, 1024) on one head of 16384 rows", "passes": res}
+
+
+def hbm_passes(ra, q, k, v, ws, w, desc, reps: int = 20, cpu_seconds: float = 0.0):
     """The HBM-bound passes beside the lap: finalize over the lap's state, and block steps
     with short KV blocks (the state read and write then outweigh the MFMA work).  Each is
     timed with events on the current stream over `reps` launches; bytes are algorithmic."""
@@ -233,6 +271,9 @@ def hbm_passes(ra, q, k, v, ws, w, desc, reps: int = 20):
     res["merge_8_parts"] = {"ms": round(ms, 4), "bytes": nbytes, "GB_s": round(nbytes / ms / 1e6, 1),
                             "frac_of_8TB_s": round(nbytes / ms / 1e6 / PEAK_HBM_GBS, 3)}
     del parts
+    if cpu_seconds > 0:
+        log("[bench] timing the oracle's HBM-bound passes on host cores")
+        res["cpu_oracle"] = cpu_hbm_baselines(d, cpu_seconds)
     return res
 
 
@@ -444,7 +485,7 @@ def main() -> int:
     side_cpu = 0.0 if args.no_cpu_baseline else 5.0
     if args.hbm_passes or every:
         log("[bench] HBM-bound passes: finalize, short KV blocks, state merge")
-        hbm = hbm_passes(ra, qd, kb[0], vb[0], ws, w, desc)
+        hbm = hbm_passes(ra, qd, kb[0], vb[0], ws, w, desc, cpu_seconds=side_cpu / 4)
     if args.backward or every:
         log("[bench] backward lap")
         bwd = backward_lap(ra, qd, kb, vb, out, lse, w, rank, mask, order, step_flops, args.steps, side_cpu)
