@@ -286,7 +286,9 @@ int ra_tile_classes(const ra_desc* desc, int32_t kv_len, int32_t mask_kind,
  * block (rank - s) mod P is copied into one of two receive buffers with hipMemcpyAsync
  * on side_stream while the previous step's kernel runs on desc.stream; events order
  * copy-after-consume and compute-after-arrival ("GPU ring attention", section "Hiding the
- * ring behind the GEMMs"; charlestar page, section 双缓冲是重叠成立的基础).
+ * ring behind the GEMMs"; charlestar page, section 双缓冲是重叠成立的基础).  Every block is
+ * received, as a ring rank forwards each one; a block that no query of the rank sees
+ * launches nothing, and its buffer is free again as soon as it has landed.
  * recv_k[2], recv_v[2] are the receive buffers (block_bytes each).  Positions follow
  * mask_kind (contiguous: rank * q_len and j * kv_len; striped and zigzag: rank and j).
  * Writes O and lse as ra_finalize does; stats_out (host, may be NULL) receives the lap's
