@@ -20,9 +20,9 @@
 //      operands by ds_read_b64_tr_b16).  Each walks the query rows of every query head that
 //      reads its KV head.  Splitting dV from dK recomputes the scores once more but halves
 //      the streamed operand bytes per matrix instruction.
-// Streamed tiles are 32 rows, double-buffered, copied straight from HBM into LDS with
-// buffer_load ... lds; one XOR swizzle per tile serves the 16-byte operand reads (conflict
-// free) and the transposing reads (at most two-way conflicts).  Each output has one owner: no
+// Streamed tiles are 32 or 64 rows, double-buffered, copied straight from HBM into LDS with
+// buffer_load ... lds; one XOR swizzle per tile keeps both the 16-byte operand reads and the
+// transposing reads free of bank conflicts.  Each output has one owner: no
 // atomics.  Only tiles holding an allowed pair are visited; the element mask runs on every
 // visited tile (cheap next to the five products).
 
@@ -48,11 +48,17 @@ constexpr int WR = 32;      // rows (dq) or keys (dkdv) per wave
 constexpr int BO = 4 * WR;  // owned per workgroup
 constexpr float kLog2e = 1.4426950408889634f;
 
-// physical 16-byte chunk of logical chunk c of tile row t
+// physical 16-byte chunk of logical chunk c of tile row t.  A tile here is read both ways:
+// 16-byte operand reads (16 lanes at a time: 16 consecutive rows at one chunk) and
+// transposing ds_read_b64_tr_b16 reads (32 lanes at a time: 4 consecutive rows, aligned,
+// x 4 consecutive chunks, aligned).  The twist puts both on distinct banks of the 64: over 16
+// consecutive rows it takes 16 distinct values (at d = 64, where a bank line holds two rows,
+// 8 distinct values per row parity), and over 4 aligned rows it moves the 4-chunk group to 4
+// disjoint groups.
 template <int D>
 __device__ __forceinline__ int phys(int t, int c) {
-  if constexpr (D == 128) return c ^ (t & 15);
-  else return c ^ ((t >> 1) & 7);
+  if constexpr (D == 128) return c ^ (4 * (t & 3) + ((t >> 2) & 3));
+  else return c ^ (4 * ((t >> 1) & 1) + ((t >> 2) & 3));
 }
 
 __device__ __forceinline__ void load_lds_b128_bwd(__amdgpu_buffer_rsrc_t r, void* lds, int voff, int soff) {
