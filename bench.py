@@ -319,9 +319,65 @@ def decode_passes(ra, reps: int = 20, cpu_seconds: float = 0.0):
                 "frac_of_8TB_s": round(nbytes / ms / 1e6 / PEAK_HBM_GBS, 3),
                 "tiled_step_ms": round(ms_tiled, 4), "speedup_vs_tiled": round(ms_tiled / ms, 2)}
             del k, v, ws
+    res.update(decode_lap_graph(ra, reps))
     if cpu_seconds > 0:
         log("[bench] timing the oracle decode update on host cores")
         res["cpu_oracle"] = cpu_decode_baseline(cpu_seconds)
+    return res
+
+
+def decode_lap_graph(ra, reps: int = 20, P: int = 8, nk: int = 16384):
+    """A whole decode lap (P blocks of nk keys through ra_decode_step, then ra_finalize; the
+    newest tokens at the end of the context, causal) issued eagerly from Python, against the
+    same lap captured once in a HIP graph on the state's stream and replayed.  Short blocks
+    leave the GPU waiting on the host's launches; the graph removes that wait."""
+    import torch
+    import synth
+    B, Hq, Hkv, d = 1, 64, 8, 128
+    N = P * nk
+    res = {}
+    s = torch.cuda.Stream()
+    for n_q in (1, 8):
+        q = synth.draw_device(6, synth.Q_ID, 0, B, Hq, n_q, d, 1 / math.sqrt(128), "bf16", "cuda")
+        k = synth.draw_device(6, synth.K_ID, -1, B, Hkv, N, d, 1 / math.sqrt(128), "bf16", "cuda")
+        v = synth.draw_device(6, synth.V_ID, -1, B, Hkv, N, d, 1 / math.sqrt(128), "bf16", "cuda")
+        kb = [k[:, :, j * nk:(j + 1) * nk] for j in range(P)]
+        vb = [v[:, :, j * nk:(j + 1) * nk] for j in range(P)]
+        desc = ra.desc_for(q, kb[0], P, stream=s)
+        ws = torch.empty(ra.decode_workspace_bytes(desc, nk), dtype=torch.uint8, device="cuda")
+        state_ws = torch.empty(ra.workspace_bytes(desc), dtype=torch.uint8, device="cuda")
+        out = torch.empty((B, Hq, n_q, d), dtype=torch.float32, device="cuda")
+        lse = torch.empty((B, Hq, n_q), dtype=torch.float32, device="cuda")
+        q_off = N - n_q
+
+        def lap():
+            st = ra.RingState(q, kb[0], ring_size=P, stream=s, workspace=state_ws)
+            for j in range(P - 1, -1, -1):        # the diagonal block first, as rank P-1 visits them
+                st.decode_step(kb[j], vb[j], 1, q_off, j * nk, workspace=ws)
+            st.finalize(out=out, lse=lse)
+            st.close()
+
+        def timed(fn):
+            with torch.cuda.stream(s):
+                fn()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(s)
+                for _ in range(reps):
+                    fn()
+                e1.record(s)
+            s.synchronize()
+            return e0.elapsed_time(e1) / reps
+
+        ms_eager = timed(lap)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            lap()
+        ms_graph = timed(g.replay)
+        kv_bytes = 2 * B * Hkv * N * d * 2
+        res[f"decode_lap_q{n_q}_p{P}x{nk}"] = {
+            "eager_ms": round(ms_eager, 4), "graph_ms": round(ms_graph, 4),
+            "graph_kv_GB_s": round(kv_bytes / ms_graph / 1e6, 1), "blocks": P, "keys_per_block": nk}
+        del g
     return res
 
 
