@@ -251,28 +251,41 @@ int make_state(const ra_desc* d, const void* q, void* ws, int fresh, ra_state** 
   return RA_OK;
 }
 
-// The split-KV step: enough key chunks that the whole chip streams the block, none shorter
-// than kDecodeMinChunk keys per wave so that a wave's fixed cost stays small next to its
-// loads.  decode_kernel aims at 2048 waves (two per SIMD); decode_ring_kernel's four-wave
-// workgroups hold an 80 KB LDS ring each and aim at 512 of them (two per CU).
-constexpr int64_t kDecodeTargetWaves = 2048;
+// The split-KV step: enough key chunks that the whole chip streams the block, none so short
+// that a wave's fixed cost or the chunk states outweigh its share of K and V.  Every chunk
+// writes, and the combine reads back, 4 (d + 2) bytes per packed row, so the more rows a
+// wave packs, the longer its chunks pay.  decode_kernel aims at 1024 waves (one per SIMD),
+// or 2048 (two per SIMD) when a lone row group packs at most 8 rows (one token of an 8:1
+// group) and its chunk states are cheap; chunks are at least kDecodeMinChunk keys per wave.
+// decode_ring_kernel's four-wave workgroups hold an 80 KB LDS ring each and aim at 512 of
+// them (two per CU), with chunks of at least kDecodeMinChunkRing keys per tile subset.
+constexpr int64_t kDecodeTargetWaves = 1024;
+constexpr int64_t kDecodeTargetWavesFewRows = 2048;
+constexpr int64_t kDecodeFewRows = 8;
 constexpr int64_t kDecodeTargetRings = 512;
 constexpr int32_t kDecodeMinChunk = 256;
+constexpr int32_t kDecodeMinChunkRing = 512;
 
 struct DecodePlan {
   int32_t n_parts, chunk;
 };
 
+// query rows that share one KV head: (query head of the group, token) pairs
+int64_t decode_packed_rows(const ra_desc* d) { return (int64_t)(d->q_heads / d->kv_heads) * d->q_len; }
+
 int64_t decode_row_groups(const ra_desc* d) {
-  const int64_t packed = (int64_t)(d->q_heads / d->kv_heads) * d->q_len;
-  return (packed + ra::kDecodeRows - 1) / ra::kDecodeRows;
+  return (decode_packed_rows(d) + ra::kDecodeRows - 1) / ra::kDecodeRows;
 }
+
+int32_t decode_min_chunk(ra::DecodeShape sh) { return sh.ring ? kDecodeMinChunkRing : kDecodeMinChunk; }
 
 // key chunks wanted per (batch, KV head, workgroup of row groups)
 int64_t decode_want(const ra_desc* d, ra::DecodeShape sh) {
   const int64_t n_wg = (decode_row_groups(d) + sh.R - 1) / sh.R;
   const int64_t base = (int64_t)d->batch * d->kv_heads * n_wg * (sh.ring ? 1 : sh.R);
-  const int64_t target = sh.ring ? kDecodeTargetRings : kDecodeTargetWaves;
+  const int64_t target = sh.ring ? kDecodeTargetRings
+                         : decode_packed_rows(d) <= kDecodeFewRows ? kDecodeTargetWavesFewRows
+                                                                   : kDecodeTargetWaves;
   return base >= target ? 1 : (target + base - 1) / base;
 }
 
@@ -283,7 +296,8 @@ DecodePlan decode_plan(const ra_desc* d, ra::DecodeShape sh, int32_t n_keys) {
   const int64_t step = (int64_t)ra::kDecodeTileK * sh.S;
   int64_t chunk = (n_keys + want - 1) / want;
   chunk = (chunk + step - 1) / step * step;
-  if (chunk < (int64_t)kDecodeMinChunk * sh.S) chunk = (int64_t)kDecodeMinChunk * sh.S;
+  const int64_t min_chunk = (int64_t)decode_min_chunk(sh) * sh.S;
+  if (chunk < min_chunk) chunk = min_chunk;
   pl.chunk = (int32_t)chunk;
   pl.n_parts = (int32_t)((n_keys + chunk - 1) / chunk);
   return pl;
@@ -296,12 +310,13 @@ struct DecodeLayout {
 // Partial states of a block of kv_len keys.  A causal block plans over its visible keys
 // n_keys <= kv_len, and the shape may change with n_keys (two row groups), so the bound is the
 // larger over the shapes n_keys can take.  For one shape, n_parts <= want and
-// n_parts <= ceil(n_keys / (S * kDecodeMinChunk)), both non-decreasing in n_keys, and each
+// n_parts <= ceil(n_keys / (S * its minimum chunk)), both non-decreasing in n_keys, and each
 // part leaves S partial states.
 DecodeLayout decode_layout(const ra_desc* d, int32_t kv_len) {
   const int64_t n_rg = decode_row_groups(d);
   auto bound = [&](ra::DecodeShape sh) {
-    int64_t parts = ((int64_t)kv_len + sh.S * kDecodeMinChunk - 1) / (sh.S * kDecodeMinChunk);
+    const int64_t per_part = (int64_t)sh.S * decode_min_chunk(sh);
+    int64_t parts = ((int64_t)kv_len + per_part - 1) / per_part;
     const int64_t want = decode_want(d, sh);
     return (parts > want ? want : parts) * sh.S;
   };

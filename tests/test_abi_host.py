@@ -348,12 +348,12 @@ def test_one_hip_runtime_per_process():
 
 
 def test_decode_workspace_bytes():
-    # chunk states of rows * (d + 2) floats, each section 256-byte aligned.  One row group of
-    # 32 packed rows per KV head: min(ceil(2048 / (B * Hkv)), ceil(kv_len / 256)) parts.
-    # Two row groups: below 131072 keys min(ceil(2048 / (B * Hkv * 2)), ceil(kv_len / 256));
-    # from there the larger of that and 2 * min(ceil(512 / (B * Hkv)), ceil(kv_len / 512)).
-    # More: R = 4 row groups per workgroup, min(ceil(512 / (B * Hkv * ceil(groups / 4))),
-    # ceil(kv_len / 256)) parts.
+    # chunk states of rows * (d + 2) floats, each section 256-byte aligned.  One row group per
+    # KV head: min(ceil(T / (B * Hkv)), ceil(kv_len / 256)) parts, T = 2048 waves for at most
+    # 8 packed rows, else 1024.  Two row groups: below 131072 keys
+    # min(ceil(1024 / (B * Hkv * 2)), ceil(kv_len / 256)); from there the larger of that and
+    # 2 * min(ceil(512 / (B * Hkv)), ceil(kv_len / (2 * 512))).  More: R = 4 row groups per
+    # workgroup, min(ceil(512 / (B * Hkv * ceil(groups / 4))), ceil(kv_len / 512)) parts.
     lib = ra.lib()
     d = _desc(q_len=1, q_heads=64, kv_heads=8)            # 8 packed rows per KV head: one group
     rows = 64
@@ -377,11 +377,15 @@ def test_decode_workspace_bytes():
     assert lib.ra_decode_workspace_bytes(C.byref(d2), 600) == states(3, 80)
     assert lib.ra_decode_workspace_bytes(C.byref(d2), 300) == states(2, 80)
     d4 = _desc(q_len=4, q_heads=64, kv_heads=4)           # 64 packed rows, 4 KV heads
-    assert lib.ra_decode_workspace_bytes(C.byref(d4), 1 << 17) == states(max(256, 2 * 128), 64 * 4)
-    assert lib.ra_decode_workspace_bytes(C.byref(d4), 1 << 20) == states(max(256, 2 * 128), 64 * 4)
+    assert lib.ra_decode_workspace_bytes(C.byref(d4), 1 << 17) == states(max(128, 2 * 128), 64 * 4)
+    assert lib.ra_decode_workspace_bytes(C.byref(d4), 1 << 20) == states(max(128, 2 * 128), 64 * 4)
+    assert lib.ra_decode_workspace_bytes(C.byref(d4), 5000) == states(20, 64 * 4)
     d3 = _desc(q_len=24, q_heads=64, kv_heads=8)          # 192 packed rows: six groups, two workgroups
     assert lib.ra_decode_workspace_bytes(C.byref(d3), 1 << 20) == states(-(-512 // (8 * 2)), 64 * 24)
-    assert lib.ra_decode_workspace_bytes(C.byref(d3), 1000) == states(4, 64 * 24)
+    assert lib.ra_decode_workspace_bytes(C.byref(d3), 1000) == states(2, 64 * 24)
+    d5 = _desc(q_len=2, q_heads=64, kv_heads=8)           # 16 packed rows: one group, 1024 waves
+    assert lib.ra_decode_workspace_bytes(C.byref(d5), 1 << 20) == states(128, 128)
+    assert lib.ra_decode_workspace_bytes(C.byref(d5), 3000) == states(12, 128)
     bad = _desc(q_len=1, d=96)
     assert lib.ra_decode_workspace_bytes(C.byref(bad), 1000) == 0
 
