@@ -584,41 +584,42 @@ __global__ __launch_bounds__(64 * R * S) __attribute__((amdgpu_waves_per_eu(2)))
   }
 }
 
-// One workgroup per state row: the maximum over the parts (and the state unless fresh), then
-// l = sum_s 2^(m_s - m) l_s and O~ = sum_s 2^(m_s - m) O~_s, each thread summing one float4
-// column over a strided subset of the parts, and the subsets added through LDS.
+// One workgroup per state row, in one pass over the parts.  Thread (pl, c) folds float4
+// column c of parts pl, pl + PL, ... into a running state of its own (m_t, l_t, O~_t): a batch
+// of U parts is loaded, the reference moves to the batch maximum if that is larger (rescaling
+// l_t and O~_t by 2^(m_t - m_new)), and each part is added with weight 2^(m_s - m_t).  The PL
+// running states of a column then merge the same way through LDS, with the lap's running state
+// folded in unless the state is fresh.  m_t is the same for every column of one pl, since the
+// parts' m values are per row.  Empty parts (m = -inf) weigh nothing.
 template <int D>
 __global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
   constexpr int C4 = D / 4;      // float4 columns of a row
   constexpr int PL = 256 / C4;   // parts summed side by side
-  __shared__ float red[256];
+  constexpr int U = 8;           // parts per batch, all loads issued before any is used
   __shared__ float4 acc_s[PL][C4];
-  __shared__ float l_s[PL];
+  __shared__ float l_s[PL], m_s[PL];
   const int tid = threadIdx.x;
   const int c = tid % C4, pl = tid / C4;
   for (int64_t row = blockIdx.x; row < p.rows; row += gridDim.x) {
-    float mx = -INFINITY;
-    for (int s = tid; s < p.n_parts; s += 256) mx = fmaxf(mx, p.part_m[(int64_t)s * p.rows + row]);
-    if (!p.fresh && tid == 0) mx = fmaxf(mx, p.m[row]);
-    red[tid] = mx;
-    __syncthreads();
-    for (int w = 128; w > 0; w >>= 1) {
-      if (tid < w) red[tid] = fmaxf(red[tid], red[tid + w]);
-      __syncthreads();
-    }
-    const float M = red[0];
+    float mt = -INFINITY, lt = 0.f;
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    float ls = 0.f;
-    auto add = [&](float ms, float l, float4 x) {
-      const float w = ms == -INFINITY ? 0.f : exp2f(ms - M);
+    auto raise_to = [&](float m_new) {   // m_new >= mt, finite
+      const float a = exp2f(mt - m_new);  // 0 while mt = -inf
+      acc.x *= a;
+      acc.y *= a;
+      acc.z *= a;
+      acc.w *= a;
+      lt *= a;
+      mt = m_new;
+    };
+    auto add = [&](float ms, float l, float4 x) {   // ms <= mt
+      const float w = ms == -INFINITY ? 0.f : exp2f(ms - mt);
       acc.x += w * x.x;
       acc.y += w * x.y;
       acc.z += w * x.z;
       acc.w += w * x.w;
-      ls += w * l;
+      lt += w * l;
     };
-    // U parts per pass, all loads issued before any is used
-    constexpr int U = 8;
     int s = pl;
     for (; s + (U - 1) * PL < p.n_parts; s += U * PL) {
       float ms[U], lv[U];
@@ -630,33 +631,54 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
         lv[u] = p.part_l[pr];
         x[u] = *reinterpret_cast<const float4*>(p.part_o + pr * D + 4 * c);
       }
+      float bm = ms[0];
+#pragma unroll
+      for (int u = 1; u < U; ++u) bm = fmaxf(bm, ms[u]);
+      if (bm > mt) raise_to(bm);
 #pragma unroll
       for (int u = 0; u < U; ++u) add(ms[u], lv[u], x[u]);
     }
     for (; s < p.n_parts; s += PL) {
       const int64_t pr = (int64_t)s * p.rows + row;
-      add(p.part_m[pr], p.part_l[pr], *reinterpret_cast<const float4*>(p.part_o + pr * D + 4 * c));
+      const float ms = p.part_m[pr];
+      if (ms > mt) raise_to(ms);
+      add(ms, p.part_l[pr], *reinterpret_cast<const float4*>(p.part_o + pr * D + 4 * c));
     }
-    if (!p.fresh && pl == 0) add(p.m[row], p.l[row], *reinterpret_cast<const float4*>(p.o_acc + row * D + 4 * c));
+    if (!p.fresh && pl == 0) {
+      const float ms = p.m[row];
+      if (ms > mt) raise_to(ms);
+      add(ms, p.l[row], *reinterpret_cast<const float4*>(p.o_acc + row * D + 4 * c));
+    }
     acc_s[pl][c] = acc;
-    if (c == 0) l_s[pl] = ls;
+    if (c == 0) {
+      l_s[pl] = lt;
+      m_s[pl] = mt;
+    }
     __syncthreads();
     if (pl == 0) {
-      for (int u = 1; u < PL; ++u) {
-        const float4 x = acc_s[u][c];
-        acc.x += x.x;
-        acc.y += x.y;
-        acc.z += x.z;
-        acc.w += x.w;
+      float M = m_s[0];
+      for (int u = 1; u < PL; ++u) M = fmaxf(M, m_s[u]);
+      acc = make_float4(0.f, 0.f, 0.f, 0.f);
+      float ls = 0.f;
+      if (M != -INFINITY) {
+        for (int u = 0; u < PL; ++u) {
+          const float mu = m_s[u];
+          const float w = mu == -INFINITY ? 0.f : exp2f(mu - M);
+          const float4 x = acc_s[u][c];
+          acc.x += w * x.x;
+          acc.y += w * x.y;
+          acc.z += w * x.z;
+          acc.w += w * x.w;
+          ls += w * l_s[u];
+        }
       }
       *reinterpret_cast<float4*>(p.o_acc + row * D + 4 * c) = acc;
       if (c == 0) {
-        for (int u = 1; u < PL; ++u) ls += l_s[u];
         p.m[row] = M;
         p.l[row] = ls;
       }
     }
-    __syncthreads();   // red, acc_s and l_s are reused by the next row
+    __syncthreads();   // acc_s, l_s and m_s are reused by the next row
   }
 }
 
