@@ -59,6 +59,9 @@ CASES = [
     (1, 8, 1, 6, 64, 140000, CONTIG, 1, 100000, 0),   # long block, but only 100006 keys visible
     (1, 8, 1, 6, 64, 133000, NONE, 1, 0, 0),          # two row groups, ring at d = 64
     (2, 8, 1, 12, 128, 5000, STRIPED, 4, 19997, 2),   # batch 2, three row groups on the ring
+    (1, 64, 8, 16, 128, 16461, CONTIG, 1, 16445, 0),  # ring chunks at their 512-key floor, 77-key tail
+    (1, 64, 8, 8, 128, 33000, NONE, 1, 0, 0),         # two row groups, 1024 waves, ragged chunks
+    (1, 64, 8, 2, 128, 20000, NONE, 1, 0, 0),         # 16 packed rows: one group, 1024-wave target
 ]
 
 
