@@ -48,6 +48,12 @@
  *    the library never allocates or frees device memory.  Host pointers are marked.
  *  - All device work is enqueued asynchronously on desc.stream (a hipStream_t; NULL is
  *    the null stream).  Device faults surface at the caller's next synchronisation.
+ *  - The state, forward, decode, finalize, merge and backward calls only launch kernels on
+ *    desc.stream: no allocation, memset, event or synchronisation.  A lap of them can be
+ *    captured in a HIP graph once its buffers exist.  Host-side state (the fresh flag, the
+ *    planner's counts) advances at capture, so a graph captured from a fresh state
+ *    recomputes the whole lap on every replay.  ra_ring_lap_emulated uses events, a second
+ *    stream and, with poison set, memsets.
  *  - Return value: RA_OK (0) or a negative RA_E_* code; nothing is enqueued on error.
  *    No C++ exception crosses the ABI.  ra_status_string() gives the text, including
  *    the HIP error for RA_E_HIP (kept per host thread).
