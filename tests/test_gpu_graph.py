@@ -1,9 +1,10 @@
 """Laps captured in a HIP graph (torch.cuda.CUDAGraph on the state's stream) and replayed.
 Every entry point that a lap calls only launches kernels on the state's stream: no
 allocation, no memset, no synchronisation.  A lap therefore captures whole: the split-KV
-decode lap, the tiled forward lap and the backward lap.  Each graph is replayed several
-times, with eager work of the program between replays, and every replay must reproduce the
-eager lap bit for bit; the eager lap itself is checked against the fp64 oracle."""
+decode lap, the tiled forward lap, the backward lap and a split-KV merge.  Each graph is
+replayed several times, with eager work of the program between replays, and every replay
+must reproduce the eager run bit for bit; the eager run itself is checked against the fp64
+oracle."""
 
 import numpy as np
 import pytest
@@ -170,3 +171,60 @@ def test_backward_lap_graph_replays_match_eager():
             assert torch.equal(dvs_g[j], dvs_e[j]), f"replay {r}: dV of block {j} differs"
         _eager_noise(qd)
     bw_g.close()
+
+
+def test_split_kv_merge_graph_replays_match_eager():
+    """Shard states over ragged key ranges, then ra_merge_states into a merged state and O, lse:
+    the steps and the merge captured whole on one stream."""
+    import exact_long_context_amd as ra
+    Hq, Hkv, n, d = 8, 2, 3, 128
+    cuts = [0, 700, 701, 1900, 2600]
+    N = cuts[-1]
+    say(f"  graph merge: {len(cuts) - 1} shard states over {N} keys")
+    q, k, v = synth.random_case(961, 1, Hq, Hkv, n, N, d, "bf16")
+    qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+    s = torch.cuda.Stream()
+    desc = ra.desc_for(qd, kd, 1, stream=s)
+    nbytes = ra.workspace_bytes(desc)
+    part_ws = [torch.empty(nbytes, dtype=torch.uint8, device="cuda") for _ in cuts[:-1]]
+    merged = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+
+    def run(out, lse):
+        sts = []
+        for w, a, b in zip(part_ws, cuts[:-1], cuts[1:]):
+            st = ra.RingState(qd, kd, stream=s, workspace=w)
+            st.step(kd[:, :, a:b], vd[:, :, a:b], NONE)
+            sts.append(st)
+        ra.merge_states(desc, part_ws, merged=merged, out=out, lse=lse)
+        return sts
+
+    out_e = torch.empty((1, Hq, n, d), dtype=torch.float32, device="cuda")
+    lse_e = torch.empty((1, Hq, n), dtype=torch.float32, device="cuda")
+    merged.fill_(0xEE)                                 # the layout's padding is never written
+    with torch.cuda.stream(s):
+        for st in run(out_e, lse_e):
+            st.close()
+    s.synchronize()
+    merged_e = merged.clone()
+    ref, ref_lse = oracle.dense_attention(to64(q), to64(k), to64(v), np.arange(n), np.arange(N), False)
+    assert_bf16_close(to64(out_e), ref, "eager merged O")
+    assert np.max(np.abs(to64(lse_e) - ref_lse)) <= 2e-2
+
+    out_g = torch.full_like(out_e, float("nan"))
+    lse_g = torch.full_like(lse_e, float("nan"))
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        sts = run(out_g, lse_g)
+    for r in range(REPLAYS):
+        with torch.cuda.stream(s):
+            out_g.fill_(float("nan"))
+            merged.fill_(0xEE)
+            for w in part_ws:
+                w.fill_(0x5A)
+            g.replay()
+        s.synchronize()
+        assert torch.equal(out_g, out_e) and torch.equal(lse_g, lse_e), f"replay {r}: O or lse differs"
+        assert torch.equal(merged, merged_e), f"replay {r}: merged state differs"
+        _eager_noise(qd)
+    for st in sts:
+        st.close()
