@@ -565,6 +565,7 @@ int ra_decode_step(ra_state* st, const void* k, const void* v, int32_t kv_len, i
   p.chunk = pl.chunk;
   p.diag = b.diag;
   p.scale_log2 = d->softmax_scale * 1.4426950408889634f;
+  p.dbg_moves = st->dbg ? st->dbg + 3 : nullptr;
   hipStream_t stream = static_cast<hipStream_t>(d->stream);
   // the row groups of one KV head share each chunk's tiles inside one workgroup
   hipError_t e = ra::launch_decode(p, d->head_dim, shape, stream);

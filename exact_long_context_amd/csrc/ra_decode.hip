@@ -87,9 +87,12 @@ __device__ __forceinline__ void pair32_dec(float x, float& a, float& b) {
 // product), and the row sum adds the same rounded values.
 constexpr float kDecodeSumMax = 4294967296.0f;   // 2^32
 
+// moves (wave-uniform) counts, twice over (both lanes of a row), the rows that already held
+// keys and moved their reference here: the debug count of the rescale by 2^(m_old - m_new).
 template <int VB>
 __device__ __forceinline__ void tile_update(f32x16& s, int lim, bool visible, float c2, float& m_run,
-                                            float& l_run, f32x16 (&oacc)[VB], bf16x8 (&pk)[2]) {
+                                            float& l_run, f32x16 (&oacc)[VB], bf16x8 (&pk)[2],
+                                            bool row_ok, unsigned& moves) {
 #pragma unroll
   for (int j = 0; j < 16; ++j) s[j] = (8 * (j >> 2) + (j & 3) > lim) ? -INFINITY : s[j];
   auto probs = [&](float ref) {
@@ -123,6 +126,7 @@ __device__ __forceinline__ void tile_update(f32x16& s, int lim, bool visible, fl
     // that has seen nothing holds zeros and takes 0: 2^-shift may overflow there)
     const float shift = (bad && mx != -INFINITY) ? mx * c2 - m_run : 0.f;
     const float alpha = l_run == 0.f ? 0.f : __builtin_amdgcn_exp2f(-shift);
+    moves += (unsigned)__builtin_popcountll(__builtin_amdgcn_ballot_w64(row_ok && bad && l_run != 0.f));
     l_run *= alpha;
 #pragma unroll
     for (int vb = 0; vb < VB; ++vb)
@@ -193,6 +197,7 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
   }
   const float c2 = p.scale_log2;
   float m_run = 0.f, l_run = 0.f;   // m: the finite reference of l and O~ (0 before any key)
+  unsigned moves = 0;
   f32x16 oacc[VB];
 #pragma unroll
   for (int vb = 0; vb < VB; ++vb)
@@ -268,7 +273,7 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
     // lane holds keys t0 + 8*(j/4) + 4*hi + (j%4) of packed row pr
     const int lim = min(i + p.diag, k1 - 1) - t0 - 4 * hi;
     bf16x8 pk[2];
-    tile_update(s, lim, lim + 4 * hi >= 0, c2, m_run, l_run, oacc, pk);
+    tile_update(s, lim, lim + 4 * hi >= 0, c2, m_run, l_run, oacc, pk, row_ok, moves);
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
@@ -312,6 +317,7 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
     }
   }
   wait_vmcnt<0>();   // the last prefetch (zeros past the chunk) is not left in flight
+  if (p.dbg_moves && moves && lane == 0) atomicAdd(p.dbg_moves, (unsigned long long)(moves / 2));
 
   if (row_ok) {
     const int64_t rows = (int64_t)p.batch * p.q_heads * p.n_q;
@@ -445,6 +451,7 @@ __global__ __launch_bounds__(64 * R * S) __attribute__((amdgpu_waves_per_eu(2)))
   }
   const float c2 = p.scale_log2;
   float m_run = 0.f, l_run = 0.f;   // m: the finite reference of l and O~ (0 before any key)
+  unsigned moves = 0;
   f32x16 oacc[VB];
 #pragma unroll
   for (int vb = 0; vb < VB; ++vb)
@@ -513,7 +520,7 @@ __global__ __launch_bounds__(64 * R * S) __attribute__((amdgpu_waves_per_eu(2)))
     // lane holds keys t0 + 8*(j/4) + 4*hi + (j%4) of packed row pr
     const int lim = min(i + p.diag, k1 - 1) - t0 - 4 * hi;
     bf16x8 pk[2];
-    tile_update(s, lim, lim + 4 * hi >= 0, c2, m_run, l_run, oacc, pk);
+    tile_update(s, lim, lim + 4 * hi >= 0, c2, m_run, l_run, oacc, pk, row_ok, moves);
     u32x2 va[2 * 2 * VB];   // (kk, vb, half)
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk)
@@ -566,6 +573,7 @@ __global__ __launch_bounds__(64 * R * S) __attribute__((amdgpu_waves_per_eu(2)))
     if constexpr (NB > 4) if (tt + 4 < n_tiles) step(I4{}, tt + 4);
   }
   wait_vmcnt<0>();   // the copies past the chunk (zeros) land before the workgroup's LDS is freed
+  if (p.dbg_moves && moves && lane == 0) atomicAdd(p.dbg_moves, (unsigned long long)(moves / 2));
 
   if (row_ok) {
     const int64_t rows = (int64_t)p.batch * p.q_heads * p.n_q;

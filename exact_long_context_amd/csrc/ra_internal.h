@@ -26,7 +26,8 @@ struct StepParams {
   int32_t diag;        // key t is visible to row i iff t <= i + diag
   float scale_log2;    // softmax scale * log2(e)
   int32_t fresh;       // 1: the state has never been written; start from the empty state
-  unsigned long long* dbg;  // optional device counters [3] (unmasked tiles, masked tiles, pairs)
+  unsigned long long* dbg;  // optional device counters [4]: unmasked tiles, masked tiles, pairs,
+                            // and (row, tile) events where a row holding keys moved its reference
 };
 
 struct FinalizeParams {
@@ -72,6 +73,7 @@ struct DecodeParams {
   int32_t n_parts, chunk;
   int32_t diag;
   float scale_log2;
+  unsigned long long* dbg_moves;  // optional device counter: rows holding keys that moved their reference
 };
 
 // Folds the parts of a split-KV step (and the state itself unless fresh) into the state.

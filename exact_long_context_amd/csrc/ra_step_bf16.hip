@@ -132,7 +132,7 @@ void step_bf16_kernel(StepParams p) {
   __shared__ __attribute__((aligned(16))) unsigned char k_t1[BK * D * 2];
   __shared__ __attribute__((aligned(16))) unsigned char v_t0[BK * D * 2];
   __shared__ __attribute__((aligned(16))) unsigned char v_t1[BK * D * 2];
-  __shared__ unsigned long long dbg_acc;
+  __shared__ unsigned long long dbg_acc[2];
   unsigned char* const k_tiles[2] = {k_t0, k_t1};
   unsigned char* const v_tiles[2] = {v_t0, v_t1};
 #define ktile(bufc) (k_tiles[decltype(bufc)::value])
@@ -167,7 +167,7 @@ void step_bf16_kernel(StepParams p) {
   const bool row_ok = qrow < p.n_q;
   const int64_t srow = ((int64_t)b * p.q_heads + h) * p.state_rows + qrow;
 
-  if (DEBUG && tid == 0) dbg_acc = 0;
+  if (DEBUG && tid < 2) dbg_acc[tid] = 0;
 
   // ---- staging: global -> LDS directly ------------------------------------------------
   const __bf16* kg = static_cast<const __bf16*>(p.k) + (int64_t)b * p.k_sb + (int64_t)kvh * p.k_sh;
@@ -286,6 +286,7 @@ void step_bf16_kernel(StepParams p) {
 
   const float c2 = p.scale_log2;
   unsigned long long my_pairs = 0;
+  unsigned my_moves = 0;   // tiles in which this lane's row, already holding keys, moved its reference
 
   // softmax of tile kt (scores in sacc) merged into the state, while the scores of tile
   // kt+1 (K buffer KN) go onto the matrix cores; then O~ += V^T P^T from V buffer VBF
@@ -356,6 +357,7 @@ void step_bf16_kernel(StepParams p) {
       // and this tile's probabilities are formed again
       const float shift = (bad && mx != -INFINITY) ? mx * c2 - m_run : 0.f;
       const float alpha = l_run == 0.f ? 0.f : __builtin_amdgcn_exp2f(-shift);
+      if (DEBUG && row_ok && hi == 0 && bad && l_run != 0.f) ++my_moves;
       l_run *= alpha;
 #pragma unroll
       for (int vb2 = 0; vb2 < VB; ++vb2)
@@ -404,6 +406,10 @@ void step_bf16_kernel(StepParams p) {
   __builtin_amdgcn_s_waitcnt(0x0F70);
   __syncthreads();
   scores(std::integral_constant<int, 0>{}, sa);
+  // The first step's copy of K tile 2 goes into K buffer 0, which every wave has just read
+  // for tile 0's scores: no wave may start it before all of them are done.  (Later steps
+  // refill a buffer read in the step before, behind that step's barrier.)
+  __syncthreads();
   for (int kt = 0; kt < kt_live; kt += 2) {
     step(std::integral_constant<int, 0>{}, kt, sa, sb);
     if (kt + 1 < kt_live) step(std::integral_constant<int, 1>{}, kt + 1, sb, sa);
@@ -426,12 +432,14 @@ void step_bf16_kernel(StepParams p) {
   }
 
   if (DEBUG) {
-    if (my_pairs) atomicAdd(&dbg_acc, my_pairs);
+    if (my_pairs) atomicAdd(&dbg_acc[0], my_pairs);
+    if (my_moves) atomicAdd(&dbg_acc[1], (unsigned long long)my_moves);
     __syncthreads();
     if (tid == 0) {
       atomicAdd(&p.dbg[0], (unsigned long long)kt_full);
       atomicAdd(&p.dbg[1], (unsigned long long)(kt_live - kt_full));
-      atomicAdd(&p.dbg[2], dbg_acc);
+      atomicAdd(&p.dbg[2], dbg_acc[0]);
+      atomicAdd(&p.dbg[3], dbg_acc[1]);
     }
   }
 #undef ktile

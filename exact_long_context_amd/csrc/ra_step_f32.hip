@@ -29,7 +29,7 @@ __global__ __launch_bounds__(NT) void step_f32_kernel(StepParams p) {
   constexpr int DP = D / 4;     // dims per lane
   __shared__ float ks[TK][D];
   __shared__ float vs[TK][D];
-  __shared__ unsigned long long dbg_acc[3];
+  __shared__ unsigned long long dbg_acc[4];
 
   const int tid = threadIdx.x;
   const int row = tid >> 2;     // 0..63
@@ -52,7 +52,7 @@ __global__ __launch_bounds__(NT) void step_f32_kernel(StepParams p) {
   const int kt_live = tiles_live(i0, i1, p.diag, p.n_k, TK);
   const int kt_full = tiles_full(i0, i1, p.diag, p.n_k, TK);
 
-  if (DEBUG && tid < 3) dbg_acc[tid] = 0;
+  if (DEBUG && tid < 4) dbg_acc[tid] = 0;
 
   float m_run, l_run, o[DP];
   if (p.fresh) {
@@ -79,6 +79,7 @@ __global__ __launch_bounds__(NT) void step_f32_kernel(StepParams p) {
   const float* kbase = static_cast<const float*>(p.k) + (int64_t)b * p.k_sb + (int64_t)g * p.k_sh;
   const float* vbase = static_cast<const float*>(p.v) + (int64_t)b * p.k_sb + (int64_t)g * p.k_sh;
   unsigned long long my_pairs = 0;
+  unsigned long long my_moves = 0;   // tiles in which this row, already holding keys, raised its max
 
   for (int kt = 0; kt < kt_live; ++kt) {
     const int t0 = kt * TK;
@@ -112,6 +113,7 @@ __global__ __launch_bounds__(NT) void step_f32_kernel(StepParams p) {
     const float m_new = fmaxf(m_run, mx);
     const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
     const float alpha = exp2f(m_run - m_use);
+    if (DEBUG && row_ok && part == 0 && l_run != 0.f && m_new > m_run) ++my_moves;
     l_run *= alpha;
 #pragma unroll
     for (int c = 0; c < DP; ++c) o[c] *= alpha;
@@ -137,11 +139,13 @@ __global__ __launch_bounds__(NT) void step_f32_kernel(StepParams p) {
   if (DEBUG) {
     __syncthreads();
     if (my_pairs) atomicAdd(&dbg_acc[2], my_pairs);
+    if (my_moves) atomicAdd(&dbg_acc[3], my_moves);
     __syncthreads();
     if (tid == 0) {
       atomicAdd(&p.dbg[0], (unsigned long long)kt_full);             // kt_full <= kt_live
       atomicAdd(&p.dbg[1], (unsigned long long)(kt_live - kt_full));
       atomicAdd(&p.dbg[2], dbg_acc[2]);
+      atomicAdd(&p.dbg[3], dbg_acc[3]);
     }
   }
 }

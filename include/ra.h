@@ -176,10 +176,14 @@ int ra_state_destroy(ra_state* st);
 /* Host-side counts accumulated by the planner over this state's steps. */
 int ra_get_stats(const ra_state* st, ra_stats* out);
 
-/* Debug: when counters is a device pointer to 3 zeroed uint64 values, every later step
- * of this state runs the counting variant of its kernel, which adds (atomically, on the
- * device) the tiles it computed unmasked, the tiles it computed masked and the allowed
- * pairs it actually scored.  NULL switches counting off. */
+/* Debug: when counters is a device pointer to 4 zeroed uint64 values, every later
+ * ra_block_step of this state runs the counting variant of its kernel, which adds
+ * (atomically, on the device) [0] the tiles it computed unmasked, [1] the tiles it computed
+ * masked, [2] the allowed pairs it actually scored and [3] the (query row, key tile) events
+ * in which a row that already held keys moved its reference m, rescaling l and O~ by
+ * 2^(m_old - m_new) ("Ring attention" MCQ page, body: the running output is rescaled by
+ * exp(old_max - new_max) when a new maximum appears).  ra_decode_step adds to [3] only.
+ * NULL switches counting off. */
 int ra_state_set_debug_counters(ra_state* st, uint64_t* counters);
 
 /* ---- reduction of shard states (split-KV decode) ---------------------------------- */

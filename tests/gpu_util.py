@@ -93,12 +93,12 @@ def assert_bf16_close(got, ref, what="", rowwise=BF16_ROWWISE):
     return e
 
 
-def assert_f32_close(got, ref, what=""):
+def assert_f32_close(got, ref, what="", tol=F32_REL):
     got = got.astype(np.float64)
     rel = float(np.max(np.abs(got - ref)) / max(np.max(np.abs(ref)), 1e-300))
     elem = float(np.max(np.abs(got - ref) / (np.abs(ref) + 1e-6)))
     say(f"    {what} normwise_rel={rel:.3e} elementwise={elem:.3e}")
-    assert rel <= F32_REL, (what, rel)
+    assert rel <= tol, (what, rel, tol)
     return rel
 
 
@@ -111,3 +111,84 @@ def seeded_rows(n: int, count: int, seed: int) -> np.ndarray:
     edge = list(range(min(16, n))) + list(range(max(0, n - 16), n))
     extra = rng.choice(n, size=min(count, n), replace=False).tolist()
     return np.array(sorted(set(edge + extra)), dtype=np.int64)
+
+
+def plant_score_levels(q, k, levels, q_amp: float = 8.0) -> None:
+    """Plant score structure through channel 0, in place on CPU tensors q [B, Hq, n, d] and
+    k [B, Hkv, N, d]: every query row gets q[..., 0] = q_amp and key t gets
+    k[..., t, 0] = levels[t] * sqrt(d) / q_amp (rounded to k's dtype), so that with the softmax
+    scale 1/sqrt(d) the planted part of any row's score against key t is levels[t] in natural
+    units; the other channels keep their (small) random values.  The oracle reads the same
+    rounded tensors, so the planted values need not be exact."""
+    d = q.shape[-1]
+    q[..., 0] = q_amp
+    lv = torch.from_numpy(np.asarray(levels, dtype=np.float64) * (math.sqrt(d) / q_amp))
+    k[..., :, 0] = lv.to(k.dtype)
+
+
+def ladder_levels(u: int, nk: int, rng) -> np.ndarray:
+    """Planted score levels (natural units) for the block visited at step u of a lap, built so
+    that the state's reference must move by far more than 32 (base 2) on rows that already
+    hold keys:
+      u = 0: every key near -40 (a row's first visible keys score very low);
+      u = 1: keys near 0, about 58 base-2 units above: the first tile of the launch rescales;
+      u even >= 2: keys 0..127 at the previous plateau, then every 8th key 35 units higher:
+               the rescale happens inside the launch, after visible tiles;
+      u odd >= 3: keys within a few units of the current plateau, taken without a rescale,
+               so the outputs mix several keys of the top plateau."""
+    t = np.arange(nk)
+    if u == 0:
+        return -40.0 + rng.uniform(-1.0, 0.0, nk)
+    if u == 1:
+        return rng.uniform(-1.0, 0.0, nk)
+    top = 30.0 + 35.0 * ((u - 2) // 2)          # plateau after this step
+    prev = 0.0 if u < 4 else top - 35.0 if u % 2 == 0 else top
+    lv = (prev if u % 2 == 0 else top - 3.0) + rng.uniform(-1.0, 0.0, nk)
+    if u % 2 == 0:
+        sel = (t >= 128) & (t % 8 == 3)
+        lv[sel] = top + rng.uniform(-1.0, 0.0, int(sel.sum()))
+    else:
+        sel = t % 4 == 1
+        lv[sel] = top + rng.uniform(-1.0, 2.0, int(sel.sum()))
+    return lv
+
+
+def oracle_head_rows_threaded(q64, k64, v64, q_pos, causal, rows, threads=None, budget=1 << 22):
+    """oracle.dense_attention on some rows of one head, run over a thread pool.
+
+    q64 [1, n, d], k64 / v64 [1, N, d] (numpy fp64; keys in global token order, so key t sits
+    at position t).  Rows go in chunks whose score matrix holds about ``budget`` elements;
+    for causal rows a chunk is given only the key prefix its last row may see (no key past it
+    is allowed to any row of the chunk, so the result is the same).  BLAS runs one thread per
+    pool thread.  Returns (O [len(rows), d], lse [len(rows)])."""
+    import os
+    from concurrent.futures import ThreadPoolExecutor
+
+    from threadpoolctl import threadpool_limits
+
+    rows = np.asarray(rows, dtype=np.int64)
+    q_pos = np.asarray(q_pos, dtype=np.int64)
+    N = k64.shape[1]
+    if threads is None:
+        threads = max(1, min(16, len(os.sched_getaffinity(0))))
+    def keys_seen(r):   # keys a chunk ending at local row r is given
+        return min(N, int(q_pos[r]) + 1) if causal else N
+
+    chunks = []
+    i = 0
+    while i < rows.size:   # rows ascend, so a chunk's last row sees the most keys
+        c = 1
+        while i + c < rows.size and (c + 1) * keys_seen(rows[i + c]) <= budget:
+            c += 1
+        chunks.append(rows[i:i + c])
+        i += c
+
+    def one(rc):
+        kc = keys_seen(rc[-1])
+        o, lse = oracle.dense_attention(q64[None, :, rc], k64[None, :, :kc], v64[None, :, :kc],
+                                        q_pos[rc], np.arange(kc), causal, row_chunk=rc.size)
+        return o[0, 0], lse[0, 0]
+
+    with threadpool_limits(1), ThreadPoolExecutor(threads) as ex:
+        res = list(ex.map(one, chunks))
+    return np.concatenate([r[0] for r in res]), np.concatenate([r[1] for r in res])

@@ -269,3 +269,59 @@ def test_decode_token_major_views():
     torch.cuda.synchronize()
     st.close()
     _check(o, lse, q, k, v, nk - n + np.arange(n), np.arange(nk), True, "token-major decode O")
+
+
+def _sawtooth_levels(nk, rng):
+    """Planted score levels (natural units) for a decode block: plateaus 0, 40, 80, 120 of 128
+    keys each, repeating.  Inside the 120 plateau only every 16th key reaches it (the rest stay
+    near 80), so the outputs mix a few dozen keys.  A chunk that starts low meets plateaus 40
+    or more units higher in later tiles: rows holding keys must move their reference."""
+    t = np.arange(nk)
+    seg = (t // 128) % 4
+    lv = 40.0 * seg - 3.0 * rng.uniform(0.0, 1.0, nk)
+    top = (seg == 3) & (t % 16 != 5)
+    lv[top] = 80.0 - 3.0 * rng.uniform(0.0, 1.0, int(top.sum()))
+    return lv
+
+
+# (B, Hq, Hkv, n_q, d, kv_len): one row group (decode_kernel, one wave), two row groups on a
+# short block (decode_kernel, two waves), four row groups (ring kernel 4 x 1), two row groups
+# on a long block (ring kernel 2 x 2)
+PLANTED = [
+    (1, 8, 1, 1, 128, 4096),
+    (1, 8, 1, 7, 128, 2500),
+    (1, 16, 2, 16, 128, 3001),
+    (1, 8, 1, 6, 64, 140000),
+]
+
+
+@pytest.mark.parametrize("case", PLANTED, ids=lambda c: f"h{c[1]}x{c[2]}n{c[3]}d{c[4]}k{c[5]}")
+def test_decode_live_rows_rescale_on_planted_sawtooth(case):
+    """Extreme scores in the split-KV step ("Ring Attention：把超长序列沿设备环流动", section
+    正确性测试应覆盖哪些边界): scores climb by 40 natural units from tile to tile inside a chunk,
+    so every chunk wave must rescale rows that already hold keys ("Ring attention" MCQ page,
+    body).  The debug counter proves the path ran; the result matches the oracle."""
+    import exact_long_context_amd as ra
+    from gpu_util import plant_score_levels
+    B, Hq, Hkv, n, d, nk = case
+    q, k, _ = synth.random_case(900 + nk % 89, B, Hq, Hkv, n, nk, d, "bf16", value_scale=0.3)
+    v = synth.random_case(901 + nk % 89, B, Hq, Hkv, n, nk, d, "bf16")[2]
+    plant_score_levels(q, k, _sawtooth_levels(nk, np.random.default_rng(nk)))
+    qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+    say(f"  planted decode {case}")
+    outs = []
+    for counted in (True, False):
+        st = ra.RingState(qd, kd)
+        counters = torch.zeros(4, dtype=torch.int64, device="cuda")
+        if counted:
+            st.set_debug_counters(counters)
+        st.decode_step(kd, vd, NONE)
+        outs.append(st.finalize())
+        st.close()
+        torch.cuda.synchronize()
+        if counted:
+            moves = counters[3].item()
+            say(f"    live-row reference moves: {moves}")
+            assert moves > 0, "no row that held keys moved its reference"
+    assert torch.equal(outs[0][0], outs[1][0])
+    _check(outs[1][0], outs[1][1], q, k, v, np.arange(n), np.arange(nk), False, "planted decode O")

@@ -13,7 +13,7 @@ import torch
 
 import oracle
 import synth
-from gpu_util import (assert_bf16_close, assert_f32_close, lap_with_steps, require_gpu, say,
+from gpu_util import (F32_REL, assert_bf16_close, assert_f32_close, lap_with_steps, require_gpu, say,
                       to64)
 
 pytestmark = pytest.mark.gpu
@@ -161,7 +161,7 @@ def test_mask_and_skip_decisions_bit_exact(dtype, mask):
     qd = q.cuda()
     for j in range(P):
         kp = oracle.tokens_of_rank(N, P, layout, j)
-        counters = torch.zeros(3, dtype=torch.int64, device="cuda")
+        counters = torch.zeros(4, dtype=torch.int64, device="cuda")
         st = ra.RingState(qd, kb[0], ring_size=P)
         st.set_debug_counters(counters)
         qo, ko = ra.block_offsets(mask, rank, j, n, n)
@@ -169,7 +169,7 @@ def test_mask_and_skip_decisions_bit_exact(dtype, mask):
         plan = st.stats()
         st.finalize()
         torch.cuda.synchronize()
-        c = counters.cpu().tolist()
+        c = counters.cpu().tolist()[:3]
         if mask == ZIGZAG:   # the kernel tiles each (query chunk, key chunk) pair on its own
             cl = n // 2
             cls = np.concatenate([oracle.tile_classes(q_pos[a * cl:(a + 1) * cl], kp[b * cl:(b + 1) * cl],
@@ -321,14 +321,19 @@ def test_strided_views_without_copies():
     assert_bf16_close(to64(o), ref, "token-major views")
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "f32"])
-def test_steps_are_bitwise_repeatable_across_many_workgroups(dtype):
+@pytest.mark.parametrize("dtype,nk", [("bf16", 64), ("bf16", 128), ("bf16", 256), ("bf16", 320),
+                                      ("f32", 320)])
+def test_steps_are_bitwise_repeatable_across_many_workgroups(dtype, nk):
     """The same fresh step and resumed step, twenty times over: the state (m, l, O~) must be
     bit-identical every time.  16384 rows x 16 heads fill the chip with co-resident
     workgroups, so a race between workgroups or between the waves of one (a tile buffer reused
-    too early, a read not yet landed) shows up as rows that change from run to run."""
+    too early, a read not yet landed) shows up as rows that change from run to run.  Blocks of
+    64 to 256 keys cover the bf16 kernel's first step, whose look-ahead copy refills the K
+    buffer the prologue's scores read: past the block's end those copies return zeros almost
+    at once, so a wave that started them before the others had read the buffer would corrupt
+    their first tile."""
     import exact_long_context_amd as ra
-    H, n, nk = 16, 16384, 320
+    H, n = 16, 16384
     g = torch.Generator(device="cpu").manual_seed(77)
     tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
     q = (torch.randn(1, H, n, 128, generator=g) * 0.3).to(tdt).cuda()
@@ -346,3 +351,127 @@ def test_steps_are_bitwise_repeatable_across_many_workgroups(dtype):
     for other in states[1:]:
         diff = (states[0] != other).nonzero()
         assert diff.numel() == 0, f"{diff.numel()} workspace bytes differ between identical runs"
+
+
+# ---------------------------------------------------------------------------
+# the rescale of rows that already hold keys (exp(old max - new max) on a new maximum)
+# ---------------------------------------------------------------------------
+
+def _planted_lap_inputs(dtype, mask, rank, N, P, Hq, Hkv, order, seed):
+    """Small random inputs with planted score ladders: the block visited at step u carries
+    ladder_levels(u) through channel 0, so rows' maxima climb by 35-40 natural units between
+    blocks and inside blocks."""
+    from gpu_util import ladder_levels, plant_score_levels
+    layout = LAYOUT[mask]
+    q_pos = oracle.tokens_of_rank(N, P, layout, rank)
+    q, k, v = synth.random_case(seed, 1, Hq, Hkv, q_pos.size, N, 128, dtype, value_scale=0.3)
+    v = synth.random_case(seed + 1, 1, Hq, Hkv, q_pos.size, N, 128, dtype)[2]
+    rng = np.random.default_rng(seed)
+    levels = np.zeros(N)
+    for u, j in enumerate(order):
+        kp = oracle.tokens_of_rank(N, P, layout, j)
+        levels[kp] = ladder_levels(u, kp.size, rng)
+    plant_score_levels(q, k, levels)
+    return q_pos, q, k, v
+
+
+def _assert_live_rescales_ran(q, kb, vb, rank, mask, P, order, dtype):
+    """Run the lap twice, with and without the kernels' debug counters: the counting variant
+    must report (row, tile) events in which a row holding keys moved its reference, and give
+    bit for bit the product kernel's result.  The product run also checks, from the state
+    after every step, that some rows holding keys raised m by more than 32 (base 2) in one
+    step, which only the rescale path does."""
+    import exact_long_context_amd as ra
+    counters = torch.zeros(4, dtype=torch.int64, device="cuda")
+    o_dbg, lse_dbg, _ = lap_with_steps(q, kb, vb, rank, mask, P, order=order, debug_counters=counters)
+    n = q.shape[2]
+    st = ra.RingState(q, kb[0], ring_size=P)
+    jumps = 0
+    m_prev = l_prev = None
+    for j in order:
+        st.step(kb[j], vb[j], mask, *ra.block_offsets(mask, rank, j, n, n))
+        _, m, l_ = (t.clone() for t in st.state_views())
+        if m_prev is not None:
+            live = (l_prev > 0) & torch.isfinite(m_prev)
+            jumps += int(((m - m_prev > 32.0) & live).sum().item())
+        m_prev, l_prev = m, l_
+    o, lse = st.finalize()
+    st.close()
+    torch.cuda.synchronize()
+    c = counters.cpu().tolist()
+    say(f"    live-row reference moves counted: {c[3]}; rows jumping > 32 between steps: {jumps}")
+    assert c[3] > 0, "no row that held keys moved its reference: the rescale path did not run"
+    assert jumps > 0
+    assert torch.equal(o, o_dbg) and torch.equal(lse, lse_dbg)
+    return o, lse
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("shuffled", [False, True], ids=["ring", "shuffled"])
+@pytest.mark.parametrize("mask,rank", [(NONE, 2), (CONTIG, 7), (STRIPED, 5), (ZIGZAG, 1)])
+def test_live_rows_rescale_on_planted_score_ladders(dtype, shuffled, mask, rank):
+    """Extreme scores ("Ring Attention：把超长序列沿设备环流动", section 正确性测试应覆盖哪些边界,
+    online-softmax stability at extreme scores): each row's first block scores near -40, and
+    later blocks raise the row maximum by 35-40 natural units, at a block's first tile and in
+    the middle of a launch.  Rows that already hold keys must rescale l and O~ by
+    2^(m_old - m_new) ("Ring attention" MCQ page, body)."""
+    N, P, Hq, Hkv = 4096, 8, 4, 2
+    layout = LAYOUT[mask]
+    order = oracle.ring_visit_order(P, rank)
+    if shuffled:
+        order = [int(j) for j in np.random.default_rng(100 + rank).permutation(P)]
+    q_pos, q, k, v = _planted_lap_inputs(dtype, mask, rank, N, P, Hq, Hkv, order, 31 + rank + 7 * mask)
+    kb, vb = _blocks(k, v, P, layout)
+    say(f"  planted ladders {dtype} mask={mask} rank={rank} order={order}")
+    o, lse = _assert_live_rescales_ran(q.cuda(), kb, vb, rank, mask, P, order, dtype)
+    ref, ref_lse = oracle.dense_attention(to64(q), to64(k), to64(v), q_pos, np.arange(N), mask != NONE)
+    got = to64(o)
+    assert np.isfinite(got).all()
+    if dtype == "bf16":
+        assert_bf16_close(got, ref, "O")
+    else:
+        # An fp32 score s carries a rounding error of about |s| * 2^-24 per operation, and its
+        # weight e^s inherits it as a relative error: the bound that holds for unit-scale
+        # logits (|s| up to about 5, as in the tiny exactness workload) grows linearly with
+        # the largest logit here (about 100).  A plain all-fp32 evaluation of the definition
+        # on these inputs is off by 5.7e-5 normwise.
+        kk = np.repeat(to64(k)[0], Hq // Hkv, 0)
+        s_max = float(np.max(np.abs(to64(q)[0] @ kk.transpose(0, 2, 1)))) / math.sqrt(128)
+        rel = assert_f32_close(got, ref, "O", tol=F32_REL * max(1.0, s_max / 5.0))
+        say(f"    largest |logit| {s_max:.1f}: fp32 bound {F32_REL * max(1.0, s_max / 5.0):.2e}, measured {rel:.2e}")
+    fin = np.isfinite(ref_lse)
+    assert np.array_equal(np.isfinite(to64(lse)), fin)
+    tol = (2e-2 if dtype == "bf16" else 1e-5) * max(1.0, float(np.max(np.abs(ref_lse[fin]))))
+    assert np.max(np.abs(to64(lse)[fin] - ref_lse[fin])) <= tol
+
+
+def test_live_rows_rescale_after_resume():
+    """Checkpoint after two blocks of a planted ladder, resume from a copy of the workspace
+    and finish: the resumed launches load states that hold keys and must move their
+    reference; the result is bit-identical to the uninterrupted lap and matches the oracle."""
+    import exact_long_context_amd as ra
+    N, P, rank, mask = 4096, 8, 5, STRIPED
+    order = oracle.ring_visit_order(P, rank)
+    q_pos, q, k, v = _planted_lap_inputs("bf16", mask, rank, N, P, 4, 2, order, 57)
+    kb, vb = _blocks(k, v, P, "striped")
+    qd = q.cuda()
+    n = q_pos.size
+    base, _, _ = lap_with_steps(qd, kb, vb, rank, mask, P, order=order)
+    st = ra.RingState(qd, kb[0], ring_size=P)
+    for j in order[:2]:
+        st.step(kb[j], vb[j], mask, *ra.block_offsets(mask, rank, j, n, n))
+    saved = st.workspace.clone()
+    st.close()
+    counters = torch.zeros(4, dtype=torch.int64, device="cuda")
+    st2 = ra.RingState(qd, kb[0], ring_size=P, workspace=saved, resume=True)
+    st2.set_debug_counters(counters)
+    for j in order[2:]:
+        st2.step(kb[j], vb[j], mask, *ra.block_offsets(mask, rank, j, n, n))
+    o2, _ = st2.finalize()
+    st2.close()
+    torch.cuda.synchronize()
+    say(f"  resumed lap: live-row reference moves {counters[3].item()}")
+    assert counters[3].item() > 0
+    assert torch.equal(o2, base)
+    ref, _ = oracle.dense_attention(to64(q), to64(k), to64(v), q_pos, np.arange(N), True)
+    assert_bf16_close(to64(o2), ref, "resumed O")
