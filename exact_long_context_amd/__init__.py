@@ -14,6 +14,7 @@ import ctypes as C
 import numpy as np
 
 from ._abi import (  # noqa: F401
+    RA_DECODE_NOALLOC_MAX_BYTES,
     RA_DTYPE_BF16,
     RA_DTYPE_F32,
     RA_E_HIP,
@@ -182,6 +183,14 @@ class RingState:
         check(lib().ra_decode_step(self._handle(), k.data_ptr(), v.data_ptr(), k.shape[2], mask_kind,
                                    q_offset, k_offset, workspace.data_ptr(),
                                    workspace.numel() * workspace.element_size()))
+
+    def decode_step_noalloc(self, k, v, mask_kind: int, q_offset: int = 0, k_offset: int = 0) -> None:
+        """ra_decode_step_noalloc: decode_step() with the chunk states in the library's own
+        per-device scratch (nothing is allocated, here or in the library)."""
+        if k.stride() != v.stride() or tuple(k.stride()[:3]) != tuple(self.desc.kv_strides):
+            raise ValueError("K and V must have the strides the state was created for")
+        check(lib().ra_decode_step_noalloc(self._handle(), k.data_ptr(), v.data_ptr(), k.shape[2],
+                                           mask_kind, q_offset, k_offset))
 
     def finalize(self, out=None, lse=None, want_lse: bool = True):
         import torch

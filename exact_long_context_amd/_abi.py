@@ -24,6 +24,7 @@ RA_MASK_CAUSAL_CONTIGUOUS = 1
 RA_MASK_CAUSAL_STRIPED = 2
 RA_MASK_CAUSAL_ZIGZAG = 3
 RA_MERGE_MAX_PARTS = 64
+RA_DECODE_NOALLOC_MAX_BYTES = 64 << 20
 
 RA_DTYPE_BF16 = 0
 RA_DTYPE_F32 = 1
@@ -95,6 +96,8 @@ SIGNATURES = {
     "ra_decode_workspace_bytes": (C.c_size_t, [C.POINTER(ra_desc), C.c_int32]),
     "ra_decode_step": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_int32, C.c_int32,
                                  C.c_int64, C.c_int64, C.c_void_p, C.c_size_t]),
+    "ra_decode_step_noalloc": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_int32, C.c_int32,
+                                         C.c_int64, C.c_int64]),
     "ra_bwd_workspace_bytes": (C.c_size_t, [C.POINTER(ra_desc)]),
     "ra_bwd_init": (C.c_int, [C.POINTER(ra_desc), C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
                               C.c_void_p, C.POINTER(C.c_void_p)]),

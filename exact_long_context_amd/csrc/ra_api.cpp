@@ -12,6 +12,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <new>
 
 #include "../../include/ra.h"
@@ -336,6 +337,41 @@ DecodeLayout decode_layout(const ra_desc* d, int32_t kv_len) {
 
 }  // namespace
 
+// Scratch of ra_decode_step_noalloc, for callers that cannot allocate: one copy of this
+// array per device, created with the library's code object and held until the process ends.
+// In host code its name is only a stand-in; the device address of the current device's copy
+// comes from hipGetSymbolAddress, looked up once per device and kept in g_scratch.
+static __device__ __align__(256) unsigned char scratch[RA_DECODE_NOALLOC_MAX_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices];
+
+// The device address of `scratch` on device dev (looked up with dev current, then kept).
+int scratch_on_device(int dev, void** out) {
+  if (dev < 0 || dev >= kMaxDevices) return fail(RA_E_UNSUPPORTED, "device %d is out of range", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    int cur = 0;
+    hipError_t e = hipGetDevice(&cur);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return hip_fail(e, "hipSetDevice");
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    const hipError_t back = cur != dev ? hipSetDevice(cur) : hipSuccess;
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (back != hipSuccess) return hip_fail(back, "hipSetDevice");
+    if (!ptr) return fail(RA_E_HIP, "hipGetSymbolAddress(scratch) gave a null address");
+    g_scratch[dev] = ptr;
+  }
+  *out = g_scratch[dev];
+  return RA_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 size_t ra_workspace_bytes(const ra_desc* desc) {
@@ -586,6 +622,29 @@ int ra_decode_step(ra_state* st, const void* k, const void* v, int32_t kv_len, i
   st->fresh = 0;
   add_stats(&st->stats, &s);
   return RA_OK;
+}
+
+int ra_decode_step_noalloc(ra_state* st, const void* k, const void* v, int32_t kv_len,
+                           int32_t mask_kind, int64_t q_offset, int64_t k_offset) {
+  if (!st) return fail(RA_E_INVALID, "state is NULL");
+  const ra_desc* d = &st->desc;
+  // only bf16 forms chunk states (fp32 takes ra_block_step, zigzag is rejected)
+  const bool chunked = d->dtype == RA_DTYPE_BF16 && mask_kind != RA_MASK_CAUSAL_ZIGZAG;
+  const size_t need = chunked ? ra_decode_workspace_bytes(d, kv_len) : 0;
+  if (need > RA_DECODE_NOALLOC_MAX_BYTES)
+    return fail(RA_E_UNSUPPORTED,
+                "the split-KV step needs %zu bytes of chunk states; the no-allocation entry point "
+                "holds %zu (use ra_decode_step with a workspace)",
+                need, (size_t)RA_DECODE_NOALLOC_MAX_BYTES);
+  // the device the work goes to: the stream's
+  int dev = 0;
+  hipStream_t stream = static_cast<hipStream_t>(d->stream);
+  hipError_t e = stream ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "device of desc.stream");
+  void* ws = nullptr;
+  const int rc = scratch_on_device(dev, &ws);
+  if (rc) return rc;
+  return ra_decode_step(st, k, v, kv_len, mask_kind, q_offset, k_offset, ws, RA_DECODE_NOALLOC_MAX_BYTES);
 }
 
 size_t ra_bwd_workspace_bytes(const ra_desc* desc) {

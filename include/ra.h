@@ -232,6 +232,21 @@ int ra_decode_step(ra_state* st, const void* k, const void* v, int32_t kv_len,
                    int32_t mask_kind, int64_t q_offset, int64_t k_offset, void* workspace,
                    size_t workspace_bytes);
 
+/* For callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): ra_decode_step with the chunk states in
+ * a scratch array the library holds per device (RA_DECODE_NOALLOC_MAX_BYTES, created with
+ * the library's code object on each device it runs on and held until the process ends)
+ * instead of a caller workspace.  Same arguments, result and errors as ra_decode_step,
+ * plus RA_E_UNSUPPORTED when ra_decode_workspace_bytes(desc, kv_len) exceeds the array.
+ * The device is desc.stream's.  The call allocates nothing; its first call on a device
+ * looks up that device's array (hipGetSymbolAddress).  Every call on a device shares that
+ * device's array, which keeps the last call's contents (nothing in it needs clearing: each
+ * call writes every chunk state before reading it), so calls whose work overlaps on one
+ * device (other streams, other host threads) race: serialise them. */
+#define RA_DECODE_NOALLOC_MAX_BYTES (64u << 20)
+int ra_decode_step_noalloc(ra_state* st, const void* k, const void* v, int32_t kv_len,
+                           int32_t mask_kind, int64_t q_offset, int64_t k_offset);
+
 /* ---- backward of the lap ------------------------------------------------------------ */
 
 /* The backward pass runs the same lap with gradients travelling too ("Ring Attention：把超长序
