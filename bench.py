@@ -421,6 +421,123 @@ def backward_lap(ra, q, kb, vb, out, lse, w, rank, mask, order, step_flops, laps
     return res
 
 
+def lap_timing(ring, qd, rank: int, mask: int, w, step_flops, warmup: int, laps: int, ws, out, lse):
+    """Emulated laps with HIP events around each step's launch: (ms per lap by the host clock,
+    step-kernel ms per live launch, useful TFLOP/s of the laps, of the step kernels)."""
+    import torch
+    for _ in range(warmup):
+        ring.lap(qd, rank, mask, workspace=ws, out=out, lse=lse)
+    events = []
+    for _ in range(laps):
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(2 * w.P)]
+        for e in evs:
+            e.record()
+        events.append(evs)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(laps):
+        ring.lap(qd, rank, mask, workspace=ws, out=out, lse=lse, step_events=events[i])
+    torch.cuda.synchronize()
+    lap_s = (time.perf_counter() - t0) / laps
+    live = [s for s in range(w.P) if step_flops[s] > 0]
+    kern = [events[i][2 * s].elapsed_time(events[i][2 * s + 1]) for i in range(laps) for s in live]
+    kern_ms = sum(kern) / max(len(kern), 1)
+    lap_flops = sum(step_flops)
+    return {
+        "lap_ms": round(1000.0 * lap_s, 4),
+        "useful_tflops_lap": round(lap_flops / lap_s / 1e12, 2),
+        "step_kernel_ms_mean": round(kern_ms, 4),
+        "step_kernel_tflops": round(sum(step_flops[s] for s in live) / len(live) / (kern_ms / 1e3) / 1e12, 2)
+        if live and kern_ms > 0 else None,
+        "live_steps": len(live),
+        "useful_flops_per_lap": lap_flops,
+    }
+
+
+def plan_flops(ra, desc, w, rank: int, mask: int):
+    from exact_long_context_amd.workload import useful_flops
+    order = [((rank - s) % w.P + w.P) % w.P for s in range(w.P)]
+    flops = []
+    for j in order:
+        qo, ko = ra.block_offsets(mask, rank, j, w.n_local, w.n_local)
+        flops.append(useful_flops(ra.plan_block(desc, w.n_local, mask, qo, ko)["live_pairs"], w.head_dim))
+    return order, flops
+
+
+# every other measured (workload, rank): the causal-contiguous ramp, the striped and
+# long-context GQA laps, and the zigzag layout, each timed in the bench's own launch
+# configuration (emulated lap with transfers)
+OTHER_CONFIGS = [
+    ("causal_contig_n131072_p8_h32", 0),
+    ("causal_contig_n131072_p8_h32", 7),
+    ("zigzag_n131072_p8_h32", 0),
+    ("zigzag_n131072_p8_h32", 7),
+    ("striped_n262144_p16_h32", 5),
+    ("gqa_striped_n1m_p64_h64kv8", 5),
+]
+
+
+def other_configs(ra, warmup: int = 1, laps: int = 3):
+    import torch
+    import synth
+    from exact_long_context_amd.workload import shard_blocks
+    dev = torch.device("cuda", 0)
+    res = {}
+    cache = {}
+    for name, rank in OTHER_CONFIGS:
+        w = synth.WORKLOADS[name]
+        mask = MASK_CODE[w.mask]
+        log(f"[bench] {name} rank {rank}")
+        key = (w.N, w.P, w.q_heads, w.kv_heads, w.value_scale)
+        if key not in cache:   # K and V are drawn in global order: shared by the layouts
+            cache.clear()
+            torch.cuda.empty_cache()
+            _, k, v = synth.workload_tensors(w, rank, heads_q=[])
+            cache[key] = (k.to(dev), v.to(dev))
+        kd, vd = cache[key]
+        q, _, _ = synth.workload_tensors(w, rank, heads_kv=[])
+        qd = q.to(dev)
+        kb, vb = shard_blocks(kd, vd, w.P, w.layout)
+        ring = ra.EmulatedRing(kb, vb)
+        desc = ra.desc_for(qd, kb[0], w.P)
+        ws = torch.empty(ra.workspace_bytes(desc), dtype=torch.uint8, device=dev)
+        out = torch.empty((w.batch, w.q_heads, w.n_local, w.head_dim), dtype=torch.float32, device=dev)
+        lse = torch.empty((w.batch, w.q_heads, w.n_local), dtype=torch.float32, device=dev)
+        _, flops = plan_flops(ra, desc, w, rank, mask)
+        r = lap_timing(ring, qd, rank, mask, w, flops, warmup, laps, ws, out, lse)
+        r.update({"rank": rank, "mask": w.mask, "value_scale": round(w.value_scale, 6),
+                  "pct_of_peak_lap": round(100.0 * r["useful_tflops_lap"] / PEAK_BF16_TFLOPS, 2)})
+        res[f"{name}/r{rank}"] = r
+        del ring, kb, vb, qd, ws, out, lse
+    cache.clear()
+    torch.cuda.empty_cache()
+    return res
+
+
+def copy_cost(ra, qd, kb, vb, ws, w, rank: int, mask: int, order, step_flops, laps: int, lap_kernel_ms):
+    """What the emulated ring's copies cost the step kernel: the same steps, in the same
+    process, with no transfer beside them (each block read in place from the pool)."""
+    import torch
+    n = w.n_local
+    live = [s for s in range(w.P) if step_flops[s] > 0]
+    ms = []
+    for _ in range(laps + 1):
+        st = ra.RingState(qd, kb[0], ring_size=w.P, workspace=ws)
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(2 * w.P)]
+        for s, j in enumerate(order):
+            evs[2 * s].record()
+            st.step(kb[j], vb[j], mask, *ra.block_offsets(mask, rank, j, n, n))
+            evs[2 * s + 1].record()
+        torch.cuda.synchronize()
+        ms.append([evs[2 * s].elapsed_time(evs[2 * s + 1]) for s in live])
+        st.close()
+    alone = [x for lap in ms[1:] for x in lap]
+    alone_ms = sum(alone) / len(alone)
+    return {"step_kernel_ms_with_copies": round(lap_kernel_ms, 4),
+            "step_kernel_ms_without_copies": round(alone_ms, 4),
+            "slowdown_from_copies": round(lap_kernel_ms / alone_ms, 4)}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -438,6 +555,11 @@ def main() -> int:
                     help="time the split-KV step for few query rows (decode) against 16K..1M keys")
     ap.add_argument("--hbm-passes", action="store_true",
                     help="time the HBM-bound passes (finalize, short KV blocks, state merge)")
+    ap.add_argument("--copy-cost", action="store_true",
+                    help="time the same step kernels without the ring's concurrent copies")
+    ap.add_argument("--configs", action="store_true",
+                    help="time the other measured workloads and ranks (causal-contiguous, zigzag, "
+                         "striped, long-context GQA)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -535,9 +657,12 @@ def main() -> int:
 
     # the passes beside the lap: those named by flag, else all of them on a bf16 workload
     # (none with --lap-only)
-    named = args.backward or args.decode or args.hbm_passes
+    named = args.backward or args.decode or args.hbm_passes or args.configs or args.copy_cost
     every = not args.lap_only and not named and w.dtype == "bf16"
-    hbm = bwd = dec = None
+    hbm = bwd = dec = cfgs = cost = None
+    if every or args.copy_cost:
+        log("[bench] step kernels without concurrent transfers")
+        cost = copy_cost(ra, qd, kb, vb, ws, w, rank, mask, order, step_flops, args.steps, avg_kernel_ms)
     side_cpu = 0.0 if args.no_cpu_baseline else 5.0
     if args.hbm_passes or every:
         log("[bench] HBM-bound passes: finalize, short KV blocks, state merge")
@@ -548,6 +673,10 @@ def main() -> int:
     if args.decode or every:
         log("[bench] split-KV decode steps")
         dec = decode_passes(ra, cpu_seconds=side_cpu)
+    if args.configs or every:
+        del ring, kb, vb
+        torch.cuda.empty_cache()
+        cfgs = other_configs(ra)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -594,6 +723,8 @@ def main() -> int:
             "hbm_passes": hbm,
             "backward": bwd,
             "decode": dec,
+            "copy_cost": cost,
+            "configs": cfgs,
         },
     }
     print(json.dumps(line), flush=True)
