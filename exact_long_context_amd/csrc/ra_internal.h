@@ -122,8 +122,8 @@ struct BwdParams {
 };
 
 // Tile sizes of each kernel (the planner reports and classifies with these).
-constexpr int kBf16TileQ = 128;
-constexpr int kBf16TileK = 64;
+constexpr int kBf16TileQ = 256;
+constexpr int kBf16TileK = 32;
 constexpr int kF32TileQ = 64;
 constexpr int kF32TileK = 32;
 constexpr int kDecodeRows = 32;   // packed (query head, token) rows per wave of the split-KV step

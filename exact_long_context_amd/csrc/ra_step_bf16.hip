@@ -10,32 +10,37 @@
 //     l'  = a * l + sum 2^(x - m'),   O~' = a * O~ + sum 2^(x - m') v.
 //
 // Design (gfx950, wave64, 160 KB LDS per CU):
-//  * A workgroup of 4 waves owns a 128-row query tile of one head; each wave owns 32 rows
-//    and keeps their q (as the MFMA B operand) and O~ (fp32 accumulators) in registers for
-//    the whole block.  Grid order is XCD-aware: workgroups that read the same KV head are
-//    dispatched to the same XCD, heaviest query tiles first.
-//  * Keys stream through LDS in 64-key tiles, double-buffered, copied straight from HBM
-//    with buffer_load ... lds (no registers, no VALU): the next tiles' copies are in flight
-//    while the current tile is on the matrix cores; one barrier per tile.  K runs one tile
-//    ahead of V, so the scores of tile kt+1 overlap the probabilities of tile kt.
+//  * A workgroup of 4 waves owns a 256-row query tile of one head; each wave owns 64 rows
+//    as two 32-row sub-tiles and keeps their q (MFMA B operands) and O~ (fp32 accumulators)
+//    in registers for the whole block.  Every K or V operand fragment a wave reads from LDS
+//    feeds both sub-tiles' products, so LDS delivers 512 bytes per 32x32x16 MFMA.  Two
+//    workgroups share a CU (two waves per SIMD): one wave's products run on the matrix core
+//    while the other forms its probabilities.  Grid order is XCD-aware: workgroups that read
+//    the same KV head are dispatched to the same XCD, heaviest query tiles first.
+//  * Keys stream through LDS in 32-key tiles, three buffers per tensor, copied straight
+//    from HBM with buffer_load ... lds (no registers, no VALU) two tiles ahead; one barrier
+//    per tile.
 //  * Scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16 (K from LDS
-//    as operand A, q from registers as operand B), so each lane ends up holding 16 keys of
-//    one query row per 32 keys: the row max and row sum need only in-lane work plus one
+//    as operand A, q from registers as operand B), so each lane holds 16 keys of one query
+//    row per sub-tile: the row max and row sum need only in-lane work plus one
 //    v_permlane32_swap with the partner lane.
 //  * The probabilities are rounded to bf16 in registers and reused directly as operand B of
 //    O~^T += V^T P^T.  V stays untransposed in LDS; operand A is read with
 //    ds_read_b64_tr_b16, which transposes 16-bit elements within 16-lane groups and hands
 //    each lane the keys in the permuted order the score layout produces, so no data moves
 //    between lanes.
-//  * LDS rows are XOR-swizzled in 16-byte chunks for gfx950's 64 banks, so that both the
-//    direct copies and the operand reads hit distinct banks.
+//  * LDS tiles are laid out fragment by fragment (below), so every operand read is a
+//    per-lane base plus an immediate and every group of lanes served together reads 256
+//    contiguous bytes: no bank conflicts and no address arithmetic per read.
 //  * The reference m of a row may lag its true maximum: a tile's terms 2^(x - m) are taken
-//    as they come while their row sum stays <= 2^32.  The row maximum is computed, and O~
-//    and l rescaled, only for a row past that bound or one setting its first reference,
-//    which in practice is the first visible tile of each row.
-//  * Causal skipping: the workgroup visits only the key tiles that hold an allowed pair
-//    and applies the element mask only on tiles that cross the diagonal or pass the
-//    block's end (ra_pos.h).
+//    as they come while every one of them stays <= 2^32, which one comparison of each lane's
+//    largest score per tile checks.  O~ and l are rescaled only for a row past that bound or
+//    one setting its first reference, which in practice is the first visible tile of each
+//    row; the common path is one branch-free run of probabilities and value products.
+//  * Causal skipping: the workgroup visits only the key tiles that hold an allowed pair for
+//    some of its rows, a wave computes only those that hold one for its own rows, and the
+//    element mask runs only on tiles that cross the diagonal or pass the block's end
+//    (ra_pos.h).
 
 #include <hip/hip_runtime.h>
 
@@ -50,43 +55,31 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int BQ = kBf16TileQ;
-constexpr int BK = kBf16TileK;
+constexpr int BQ = kBf16TileQ;  // 256 query rows per workgroup
+constexpr int BK = kBf16TileK;  // 32 keys per tile
 constexpr int NT = 256;         // 4 waves
-constexpr int WROWS = 32;       // query rows per wave
+constexpr int WROWS = 64;       // query rows per wave: two sub-tiles of 32
+static_assert(BQ == 4 * WROWS && BK == 32, "tile shape");
 
-
-// LDS banking on gfx950: 64 banks of 4 bytes (a 256-byte bank line).  A 16-byte-per-lane
-// access is served 16 lanes at a time and an 8-byte-per-lane access 32 lanes at a time, so
-// those lanes must touch distinct banks.
-//
-// Tiles are written straight from global memory into LDS (buffer_load ... lds: lane i of a
-// load writes bytes [16i, 16i+16) after the instruction's LDS base), so the swizzles below
-// are realised by choosing which 16-byte global chunk each lane fetches.
-
-// K tile [BK][D] bf16: physical 16-byte chunk of logical chunk c (dims 8c..8c+7) of key
-// row t.  The score operand read (16 consecutive rows at one chunk) hits 16 groups.
-template <int D>
-__device__ __forceinline__ int k_phys(int t, int c) {
-  if constexpr (D == 128) return c ^ (t & 15);
-  else return c ^ ((t >> 1) & 7);
-}
-// V tile [BK][D] bf16, kept untransposed: the value operand is read with
-// ds_read_b64_tr_b16, whose 16-lane groups fetch four consecutive keys x four 8-byte
-// column pieces; the chunk twist below puts those 16 pieces (32 lanes: 256 bytes) on
-// distinct banks.
-template <int D>
-__device__ __forceinline__ int v_phys(int t, int c) {
-  if constexpr (D == 128) return c ^ (4 * (t & 3));
-  else return c ^ (4 * ((t >> 1) & 1));
-}
+// LDS layouts.  Tiles are written straight from global memory into LDS (buffer_load ... lds:
+// lane i of a copy writes bytes [16i, 16i+16) after the instruction's LDS base), one 1 KB
+// region per copy, and each tile is laid out fragment by fragment, in the order the operand
+// reads want it:
+//  * K tile: for each 16-dim slice ks of the head dimension, 1 KB holding the 32 keys' dims
+//    16ks..16ks+7 (512 bytes, key-major) then dims 16ks+8..16ks+15.  The score operand
+//    (lane (r32, hi): key r32, dims 16ks + 8hi ..) is one 16-byte read at ks*1024 + hi*512 +
+//    r32*16: every 16 lanes read 256 contiguous bytes, all 64 banks.
+//  * V tile: for each 32-wide block vb of the value dimension, 2 KB holding the 32 keys' 64
+//    bytes of that block, key-major.  The transposing value-operand reads of a 32-lane half
+//    cover four consecutive keys' 64 bytes: 256 contiguous bytes again.
+// So every operand read is a per-lane base plus an immediate, with no swizzle; the copies in
+// turn fetch 32 (K) or 64 (V) bytes of each key row per instruction.
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) const volatile bf16x8 lds_cvbf16x8;
 
 // 16 bytes per lane from a buffer straight into LDS at lds + 16 * lane (the LDS address is
 // taken from the first lane).  Kept out of the kernel template: the builtin has no host
@@ -109,34 +102,69 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, in
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, 0x00020000);
 }
 
-// The reference m of a row may lag its true maximum: a tile's terms 2^(x - m) are used as
-// they come as long as their row sum stays <= 2^32 (so every term does), which fp32 and bf16
-// hold without loss; only a row past that, or one setting its first reference, takes the
-// tile's maximum.  Most tiles compute no maximum at all.
-constexpr float kSumMax = 4294967296.0f;   // 2^32
+// The reference of a row that has seen no key yet: any visible key's score is then more than
+// 32 (base 2) above it, so the guard sends the row to the slow path without a test of its
+// own, while masked keys (x = -inf) never trip it.
+constexpr float kNoRef = -1e30f;
 
+// max(a, b, c) in one instruction (the compiler splits fmaxf chains into two-input maxima)
+__device__ __forceinline__ float max3(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
+// s_waitcnt with vmcnt = N (six bits: [3:0] and [15:14]); expcnt and lgkmcnt not waited on
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt has six bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// The barrier between two tiles.  This wave's copies of the next tile have landed (vmcnt: all
+// but the last N copy instructions, those of the tile after it, which stay in flight) and its
+// reads of the current tile are done (lgkmcnt 0); s_barrier then publishes both to every wave.
+// __syncthreads() would also wait for the copies still in flight.  The empty asm statements
+// keep the compiler from moving LDS accesses across the barrier.
+template <int N>
+__device__ __forceinline__ void tile_barrier() {
+  static_assert(N >= 0 && N < 64, "vmcnt has six bits");
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | ((N >> 4) << 14));   // vmcnt(N) lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
 
 template <int D, bool DEBUG>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void step_bf16_kernel(StepParams p) {
   constexpr int KS = D / 16;             // k-steps of the score contraction
   constexpr int VB = D / 32;             // 32-wide blocks of the value dimension
-  constexpr int RB = D * 2;              // bytes per key row in LDS
-  constexpr int CPR = D / 8;             // 16-byte chunks per key row
-  constexpr int RPL = 64 / CPR;          // key rows per 1 KB direct load (one wave)
-  constexpr int LPW = BK * RB / 1024 / 4;  // direct loads per wave per tile, per tensor
-  // K tiles and V tiles, two of each, as separate objects so that the compiler can tell the
-  // tile being read from the one a direct load is filling.  K runs one tile ahead of V:
-  // while tile kt's probabilities are formed, tile kt+1's scores are on the matrix cores.
-  __shared__ __attribute__((aligned(16))) unsigned char k_t0[BK * D * 2];
-  __shared__ __attribute__((aligned(16))) unsigned char k_t1[BK * D * 2];
-  __shared__ __attribute__((aligned(16))) unsigned char v_t0[BK * D * 2];
-  __shared__ __attribute__((aligned(16))) unsigned char v_t1[BK * D * 2];
+  constexpr int TB = BK * D * 2;          // bytes per K or V tile
+  constexpr int KPW = KS / 4;             // K copies (1 KB each) per wave per tile
+  constexpr int VPW = 2 * VB / 4;         // V copies per wave per tile
+  constexpr int LPW = KPW + VPW;          // copies per wave per tile
+  static_assert(KPW >= 1 && VPW >= 1, "every wave copies a share of each tile");
+  // Three K and three V tile buffers, as separate objects so that the compiler can tell the
+  // tile being read from the ones direct loads are filling.  Tile kt sits in buffer kt % 3;
+  // the copies of tile kt+2 start while tile kt is computed.
+  __shared__ __attribute__((aligned(16))) unsigned char k_t0[TB];
+  __shared__ __attribute__((aligned(16))) unsigned char k_t1[TB];
+  __shared__ __attribute__((aligned(16))) unsigned char k_t2[TB];
+  __shared__ __attribute__((aligned(16))) unsigned char v_t0[TB];
+  __shared__ __attribute__((aligned(16))) unsigned char v_t1[TB];
+  __shared__ __attribute__((aligned(16))) unsigned char v_t2[TB];
+  // q fragment 0 of both sub-tiles of every wave, parked in LDS: read back once per tile,
+  // it frees 8 registers that the tile's probabilities need
+  __shared__ __attribute__((aligned(16))) unsigned char q_park[4 * 2 * 1024];
   __shared__ unsigned long long dbg_acc[2];
-  unsigned char* const k_tiles[2] = {k_t0, k_t1};
-  unsigned char* const v_tiles[2] = {v_t0, v_t1};
+  unsigned char* const k_tiles[3] = {k_t0, k_t1, k_t2};
+  unsigned char* const v_tiles[3] = {v_t0, v_t1, v_t2};
 #define ktile(bufc) (k_tiles[decltype(bufc)::value])
 #define vtile(bufc) (v_tiles[decltype(bufc)::value])
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -163,9 +191,11 @@ void step_bf16_kernel(StepParams p) {
   const int kt_full = tiles_full(i0, i1, p.diag, p.n_k, BK);
   if (!p.fresh && kt_live == 0) return;  // nothing visible: state unchanged
 
-  const int qrow = i0 + wave * WROWS + r32;
-  const bool row_ok = qrow < p.n_q;
-  const int64_t srow = ((int64_t)b * p.q_heads + h) * p.state_rows + qrow;
+  // this wave's rows [w0, w1): the key tiles it computes, and those it needs no mask on
+  const int w0 = i0 + wave * WROWS;
+  const int w1 = min(w0 + WROWS, p.n_q);
+  const int wt_live = tiles_live(w0, w1, p.diag, p.n_k, BK);
+  const int wt_full = tiles_full(w0, w1, p.diag, p.n_k, BK);
 
   if (DEBUG && tid < 2) dbg_acc[tid] = 0;
 
@@ -173,262 +203,273 @@ void step_bf16_kernel(StepParams p) {
   const __bf16* kg = static_cast<const __bf16*>(p.k) + (int64_t)b * p.k_sb + (int64_t)kvh * p.k_sh;
   const __bf16* vg = static_cast<const __bf16*>(p.v) + (int64_t)b * p.k_sb + (int64_t)kvh * p.k_sh;
   const int row_bytes = (int)(p.k_st * 2);        // host guarantees BK rows fit in 31 bits
-  // Load u of wave w covers key rows (w*LPW + u)*RPL .. +RPL-1; lane -> (row, physical
-  // chunk) = (lane / CPR, lane % CPR) of that span; the global chunk is the inverse swizzle.
-  int k_goff[LPW], v_goff[LPW];
-#pragma unroll
-  for (int u = 0; u < LPW; ++u) {
-    const int t = (wave * LPW + u) * RPL + lane / CPR;
-    const int pc = lane % CPR;
-    int ck = 0, cv = 0;   // logical chunks whose physical slot is pc (the swizzles are involutions)
-    ck = k_phys<D>(t, pc);
-    cv = v_phys<D>(t, pc);
-    k_goff[u] = (lane / CPR) * row_bytes + ck * 16;
-    v_goff[u] = (lane / CPR) * row_bytes + cv * 16;
-  }
+  // K copy ks: lane -> key lane & 31, dims 16ks + 8(lane >> 5) ..: global offset
+  // k_goff + 32ks.  V copy (vb, h): lane -> key 16h + (lane >> 2), 16-byte piece lane & 3 of
+  // block vb: v_goff + 64vb + 16h*row_bytes.  Wave w issues K copies ks = w*KPW .. and V
+  // copies 2vb + h = w*VPW ...
+  const int k_goff = (lane & 31) * row_bytes + (lane >> 5) * 16;
+  const int v_goff = (lane >> 2) * row_bytes + (lane & 3) * 16;
   auto rsrc_of = [&](const __bf16* base, int kt) {
     const int64_t t0 = (int64_t)kt * BK;
     return make_rsrc(base + t0 * p.k_st, ((int64_t)p.n_k - t0) * p.k_st * 2);
   };
-  auto load_k = [&](auto bufc, int kt) {
-    const __amdgpu_buffer_rsrc_t r = rsrc_of(kg, kt);
+  auto load_kv = [&](auto bufc, int kt) {
+    const __amdgpu_buffer_rsrc_t rk = rsrc_of(kg, kt);
+    const __amdgpu_buffer_rsrc_t rv = rsrc_of(vg, kt);
+    // the per-copy part of each offset is wave-uniform: it goes in the scalar offset, so one
+    // VGPR per tensor serves every copy
 #pragma unroll
-    for (int u = 0; u < LPW; ++u) {
-      const int row0 = (wave * LPW + u) * RPL;
-      load_lds_b128_inl(r, ktile(bufc) + row0 * RB, k_goff[u], row0 * row_bytes);
+    for (int u = 0; u < KPW; ++u) {
+      const int ks = wave * KPW + u;
+      load_lds_b128_inl(rk, ktile(bufc) + ks * 1024, k_goff, ks * 32);
     }
-  };
-  auto load_v = [&](auto bufc, int kt) {
-    const __amdgpu_buffer_rsrc_t r = rsrc_of(vg, kt);
 #pragma unroll
-    for (int u = 0; u < LPW; ++u) {
-      const int row0 = (wave * LPW + u) * RPL;
-      load_lds_b128_inl(r, vtile(bufc) + row0 * RB, v_goff[u], row0 * row_bytes);
+    for (int u = 0; u < VPW; ++u) {
+      const int c = wave * VPW + u, vb = c >> 1, h = c & 1;
+      load_lds_b128_inl(rv, vtile(bufc) + vb * 2048 + h * 1024, v_goff, vb * 64 + h * 16 * row_bytes);
     }
   };
 
   // ---- resident operands and state ---------------------------------------------------
-  bf16x8 qf[KS];
-  {
+  int qrow[2];
+  bool row_ok[2];
+  int64_t srow[2];
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    qrow[s] = w0 + 32 * s + r32;
+    row_ok[s] = qrow[s] < p.n_q;
+    srow[s] = ((int64_t)b * p.q_heads + h) * p.state_rows + qrow[s];
+  }
+  bf16x8 qf[2][KS];
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
     const __bf16* qp = static_cast<const __bf16*>(p.q) + (int64_t)b * p.q_sb +
-                       (int64_t)h * p.q_sh + (int64_t)qrow * p.q_st + hi * 8;
+                       (int64_t)h * p.q_sh + (int64_t)qrow[s] * p.q_st + hi * 8;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      if (row_ok) {
-        qf[ks] = *reinterpret_cast<const bf16x8*>(qp + ks * 16);
+      if (row_ok[s]) {
+        qf[s][ks] = *reinterpret_cast<const bf16x8*>(qp + ks * 16);
       } else {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) qf[ks][e] = (__bf16)0.0f;
+        for (int e = 0; e < 8; ++e) qf[s][ks][e] = (__bf16)0.0f;
       }
     }
   }
 
-  f32x16 oacc[VB];
-  float m_run, l_run;   // m_run: the finite reference of l and O~ (0 before any key)
-  if (p.fresh || !row_ok) {
-    m_run = 0.f;
-    l_run = 0.f;
 #pragma unroll
-    for (int vb = 0; vb < VB; ++vb)
-#pragma unroll
-      for (int j = 0; j < 16; ++j) oacc[vb][j] = 0.f;
-  } else {
-    m_run = p.m[srow];
-    l_run = p.l[srow];
-    if (m_run == -INFINITY) m_run = 0.f;
-    const float* op = p.o_acc + srow * D + 4 * hi;
-#pragma unroll
-    for (int vb = 0; vb < VB; ++vb)
-#pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        const float4 x = *reinterpret_cast<const float4*>(op + vb * 32 + 8 * a);
-        oacc[vb][4 * a + 0] = x.x;
-        oacc[vb][4 * a + 1] = x.y;
-        oacc[vb][4 * a + 2] = x.z;
-        oacc[vb][4 * a + 3] = x.w;
-      }
-  }
+  for (int s = 0; s < 2; ++s)
+    *reinterpret_cast<bf16x8*>(q_park + (wave * 2 + s) * 1024 + lane * 16) = qf[s][0];
 
-  // operand reads: loop-invariant per-lane byte offsets inside one tile
-  int k_roff[KS];   // score operand A: key row kh*32 + r32, chunk 2*ks + hi
+  f32x16 oacc[2][VB];
+  // m_run: the row's finite reference (kNoRef before any key); l_run: this lane's share of
+  // the row sum (its own keys' terms), the two lanes of a row added at the end
+  float m_run[2], l_run[2];
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) k_roff[ks] = r32 * RB + (k_phys<D>(r32, 2 * ks + hi) << 4);
-  // value operand A via ds_read_b64_tr_b16: in each 16-lane group, lane 4a+c receives
-  // element c of the 8-byte pieces addressed by lanes a, a+4, a+8, a+12.  Lane j = 16g+a+4e
-  // therefore addresses key 16*kk + 4*(g>>1) + 8*half + e, value dims
-  // 32*vb + 16*(g&1) + 4*a .. +3, which hands lane l the transposed operand for value row
-  // 32*vb + (l & 31), keys 16*kk + 4*(l>>5) + {0,1,2,3} (half 0) and +8 (half 1): the key
-  // order of the score layout.
-  int v_roff[VB];
-  {
-    const int g = lane >> 4, a = lane & 3, e = (lane >> 2) & 3;
-    const int key = 4 * (g >> 1) + e;   // + 16*kk + 8*half: multiples of 4 (immediates)
+  for (int s = 0; s < 2; ++s) {
+    if (p.fresh || !row_ok[s]) {
+      m_run[s] = kNoRef;
+      l_run[s] = 0.f;
 #pragma unroll
-    for (int vb = 0; vb < VB; ++vb) {
-      const int dv = 32 * vb + 16 * (g & 1) + 4 * a;
-      v_roff[vb] = key * RB + (v_phys<D>(key, dv >> 3) << 4) + ((dv & 7) << 1);
+      for (int vb = 0; vb < VB; ++vb)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) oacc[s][vb][j] = 0.f;
+    } else {
+      m_run[s] = p.m[srow[s]];
+      l_run[s] = hi == 0 ? p.l[srow[s]] : 0.f;
+      if (m_run[s] == -INFINITY) m_run[s] = kNoRef;
+      const float* op = p.o_acc + srow[s] * D + 4 * hi;
+#pragma unroll
+      for (int vb = 0; vb < VB; ++vb)
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          const float4 x = *reinterpret_cast<const float4*>(op + vb * 32 + 8 * a);
+          oacc[s][vb][4 * a + 0] = x.x;
+          oacc[s][vb][4 * a + 1] = x.y;
+          oacc[s][vb][4 * a + 2] = x.z;
+          oacc[s][vb][4 * a + 3] = x.w;
+        }
     }
   }
 
-  // S^T = K Q^T for the K tile in buffer B: lane holds keys 8*(j/4) + 4*hi + (j%4) (+32*kh)
-  // of query row r32
-  auto scores = [&](auto bufc, f32x16 (&sacc)[2]) {
-    const unsigned char* kt_base = ktile(bufc);
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-#pragma unroll
-      for (int kh = 0; kh < 2; ++kh) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(kt_base + k_roff[ks] + kh * 32 * RB);
-        sacc[kh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], ks == 0 ? f32x16{} : sacc[kh], 0, 0, 0);
-      }
-    }
-  };
+  // Operand reads: one per-lane base per tensor, everything else immediate.
+  //  * score operand A, fragment ks (lane (r32, hi): key r32, dims 16ks + 8hi ..):
+  //    ks*1024 + kb0;
+  //  * value operand A via ds_read_b64_tr_b16: in each 16-lane group, lane 4a+c receives
+  //    element c of the 8-byte pieces addressed by lanes a, a+4, a+8, a+12.  Lane
+  //    j = 16g+a+4e therefore addresses key 16*kk + 4*(g>>1) + 8*half + e, value dims
+  //    32*vb + 16*(g&1) + 4*a .. +3, which hands lane l the transposed operand for value row
+  //    32*vb + (l & 31), keys 16*kk + 4*(l>>5) + {0,1,2,3} (half 0) and +8 (half 1): the key
+  //    order of the score layout.  Address vb*2048 + (16kk + 8half)*64 + vb0.
+  const int kb0 = hi * 512 + r32 * 16;
+  const int vb0 = (4 * (lane >> 5) + ((lane >> 2) & 3)) * 64 + (16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * 2;
 
   const float c2 = p.scale_log2;
   unsigned long long my_pairs = 0;
-  unsigned my_moves = 0;   // tiles in which this lane's row, already holding keys, moved its reference
+  unsigned my_moves = 0;   // reference moves of this lane's rows that already held keys
 
-  // softmax of tile kt (scores in sacc) merged into the state, while the scores of tile
-  // kt+1 (K buffer KN) go onto the matrix cores; then O~ += V^T P^T from V buffer VBF
-  auto tile = [&](auto knext, auto vbuf, int kt, f32x16 (&sacc)[2], f32x16 (&snext)[2]) {
-    const unsigned char* vt_base = vtile(vbuf);
+  // One 32-key tile from buffer B: S^T = K Q^T for both sub-tiles (each K fragment feeds
+  // both), the guard on the reference, then per 16-key half the probabilities and
+  // O~^T += V^T P^T (each V fragment feeds both sub-tiles).  Working in halves keeps only 16
+  // keys' probabilities in registers.
+  auto tile = [&](auto bufc, int kt) {
+    const unsigned char* kt_base = ktile(bufc);
+    const unsigned char* vt_base = vtile(bufc);
+    f32x16 sacc[2];
+    {
+      // q fragment 0 comes back from LDS (a volatile read: the compiler may not keep it in a
+      // register across tiles, which is the point)
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(kt_base + kb0);
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const bf16x8 qb = *(lds_cvbf16x8*)(q_park + (wave * 2 + s) * 1024 + lane * 16);
+        sacc[s] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qb, f32x16{}, 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int ks = 1; ks < KS; ++ks) {
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(kt_base + ks * 1024 + kb0);
+#pragma unroll
+      for (int s = 0; s < 2; ++s)
+        sacc[s] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s][ks], sacc[s], 0, 0, 0);
+    }
     // element mask on tiles that cross the diagonal or run past the block's end
-    if ((kt >= kt_full) || ((kt + 1) * BK > p.n_k)) {
-      const int lim = min(qrow + p.diag, p.n_k - 1) - kt * BK - 4 * hi;
+    if ((kt >= wt_full) || ((kt + 1) * BK > p.n_k)) {
 #pragma unroll
-      for (int kh = 0; kh < 2; ++kh)
-#pragma unroll
-        for (int j = 0; j < 16; ++j)
-          sacc[kh][j] = (kh * 32 + 8 * (j >> 2) + (j & 3) > lim) ? -INFINITY : sacc[kh][j];
-    }
-    if (DEBUG && row_ok) {
-#pragma unroll
-      for (int kh = 0; kh < 2; ++kh)
-#pragma unroll
-        for (int j = 0; j < 16; ++j) my_pairs += (sacc[kh][j] != -INFINITY) ? 1 : 0;
-    }
-
-    // the next tile's scores: independent of everything below, so the matrix cores work
-    // on them while the vector unit forms this tile's probabilities
-    scores(knext, snext);
-
-    // probabilities 2^(x - m_run), rounded to bf16: the B operand of the value product; the
-    // row sum adds the same rounded values (v_dot2 with ones), so the weights used for O~ and
-    // for l agree exactly and a row with a single visible key normalises to exactly 1.  The
-    // sum also guards the reference: a row whose sum exceeds kSumMax grew too far above
-    // m_run, and a row that has seen nothing (l = 0) but has a visible key here must set its
-    // reference first.  Only then is the tile's maximum taken.
-    bf16x8 pk[4];
-    auto probs = [&](float shift) {
-#pragma unroll
-      for (int kh = 0; kh < 2; ++kh)
+      for (int s = 0; s < 2; ++s) {
+        const int lim = min(qrow[s] + p.diag, p.n_k - 1) - kt * BK - 4 * hi;
 #pragma unroll
         for (int j = 0; j < 16; ++j)
-          pk[2 * kh + (j >> 3)][j & 7] = (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kh][j], c2, -shift));
-      float r = 0.f;
-      const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        r = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pk[kk], pk[kk], 0, 1), ones, r, false);
-        r = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pk[kk], pk[kk], 2, 3), ones, r, false);
-        r = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pk[kk], pk[kk], 4, 5), ones, r, false);
-        r = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pk[kk], pk[kk], 6, 7), ones, r, false);
+          sacc[s][j] = (8 * (j >> 2) + (j & 3) > lim) ? -INFINITY : sacc[s][j];
       }
-      float a, bb;
-      pair32(r, a, bb);
-      return a + bb;
-    };
-    float rs = probs(m_run);
-    const bool visible = kt * BK <= qrow + p.diag;
-    const bool bad = !(rs <= kSumMax) || (l_run == 0.f && visible);
-    if (__builtin_amdgcn_ballot_w64(bad)) {
-      float mx = sacc[0][0];
+    }
+    if (DEBUG) {
 #pragma unroll
-      for (int kh = 0; kh < 2; ++kh)
+      for (int s = 0; s < 2; ++s)
+        if (row_ok[s])
 #pragma unroll
-        for (int j = 0; j < 16; ++j) mx = fmaxf(mx, sacc[kh][j]);
-      {
+          for (int j = 0; j < 16; ++j) my_pairs += (sacc[s][j] != -INFINITY) ? 1 : 0;
+    }
+
+    // The guard on the reference, once per tile and before any probability is formed: every
+    // term 2^(x - m_run) must stay <= 2^32 (fp32 and bf16 hold it without loss).  fma is
+    // monotonic in x, so it is enough that this lane's largest score passes; a row whose lane
+    // does not (or that has no reference yet: kNoRef makes any visible score fail) moves its
+    // reference to the row's maximum here, rescaling l and O~.  That is rare (in practice the
+    // first visible tile of a row), so the common path is one straight run of probabilities
+    // and value products with no branch.
+    float mx[2];
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      float a = max3(sacc[s][0], sacc[s][1], sacc[s][2]);
+#pragma unroll
+      for (int j = 3; j < 15; j += 2) a = max3(a, sacc[s][j], sacc[s][j + 1]);
+      mx[s] = fmaxf(a, sacc[s][15]);
+    }
+    const unsigned long long bad0 = __builtin_amdgcn_ballot_w64(__builtin_fmaf(mx[0], c2, -m_run[0]) > 32.f);
+    const unsigned long long bad1 = __builtin_amdgcn_ballot_w64(__builtin_fmaf(mx[1], c2, -m_run[1]) > 32.f);
+    if (bad0 | bad1) {
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const unsigned long long bad = s == 0 ? bad0 : bad1;
+        // the row is bad if either of its lanes is (lane r32 and lane r32 + 32)
+        const unsigned rows = (unsigned)bad | (unsigned)(bad >> 32);
+        const bool row_bad = (rows >> r32) & 1u;
         float a, bb;
-        pair32(mx, a, bb);
-        mx = fmaxf(a, bb);
+        pair32(mx[s], a, bb);
+        const float mrow = fmaxf(a, bb);
+        // a bad row moves its reference to its maximum: l and O~ scale by 2^(m_old - m_new),
+        // which is 0 for a row that had no reference (its O~ and l are 0 as well)
+        const float m_new = row_bad ? mrow * c2 : m_run[s];
+        const float alpha = __builtin_amdgcn_exp2f(m_run[s] - m_new);
+        if (DEBUG && row_ok[s] && hi == 0 && row_bad && m_run[s] != kNoRef) ++my_moves;
+        l_run[s] *= alpha;
+#pragma unroll
+        for (int vb = 0; vb < VB; ++vb)
+#pragma unroll
+          for (int j = 0; j < 16; ++j) oacc[s][vb][j] *= alpha;
+        m_run[s] = m_new;
       }
-      // a bad row moves its reference to the tile's maximum: l and O~ scale by 2^-shift
-      // (a row that has seen nothing holds zeros and takes 0: 2^-shift may overflow there)
-      // and this tile's probabilities are formed again
-      const float shift = (bad && mx != -INFINITY) ? mx * c2 - m_run : 0.f;
-      const float alpha = l_run == 0.f ? 0.f : __builtin_amdgcn_exp2f(-shift);
-      if (DEBUG && row_ok && hi == 0 && bad && l_run != 0.f) ++my_moves;
-      l_run *= alpha;
-#pragma unroll
-      for (int vb2 = 0; vb2 < VB; ++vb2)
-#pragma unroll
-        for (int j = 0; j < 16; ++j) oacc[vb2][j] *= alpha;
-      m_run += shift;
-      rs = probs(m_run);
     }
-    l_run += rs;
 
-    // O~^T += V^T P^T; the transposed value operand comes from two transposing reads
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
+    for (int kk = 0; kk < 2; ++kk) {
+      // probabilities 2^(x - m_run) of keys 16kk .. 16kk+15, rounded to bf16: the B operand
+      // of the value product; this lane's share of the row sum adds the same rounded values
+      // (v_dot2 with ones), so the weights used for O~ and for l agree exactly and a row with
+      // a single visible key normalises to exactly 1
+      bf16x8 pk[2];
 #pragma unroll
-      for (int vb2 = 0; vb2 < VB; ++vb2) {
-        const unsigned char* base = vt_base + v_roff[vb2] + kk * 16 * RB;
+      for (int s = 0; s < 2; ++s) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          pk[s][j] = (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(sacc[s][8 * kk + j], c2, -m_run[s]));
+        float r = l_run[s];
+        const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+        r = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pk[s], pk[s], 0, 1), ones, r, false);
+        r = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pk[s], pk[s], 2, 3), ones, r, false);
+        r = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pk[s], pk[s], 4, 5), ones, r, false);
+        r = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pk[s], pk[s], 6, 7), ones, r, false);
+        l_run[s] = r;
+      }
+
+      // O~^T += V^T P^T; the transposed value operand comes from two transposing reads
+#pragma unroll
+      for (int vb = 0; vb < VB; ++vb) {
+        const unsigned char* base = vt_base + vb * 2048 + kk * 16 * 64 + vb0;
         const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base));
-        const s16x4 hi8 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + 8 * RB));
+        const s16x4 hi8 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + 8 * 64));
         typedef short s16x8 __attribute__((ext_vector_type(8)));
         const s16x8 both = __builtin_shufflevector(lo, hi8, 0, 1, 2, 3, 4, 5, 6, 7);
         bf16x8 a;
         __builtin_memcpy(&a, &both, sizeof a);
-        oacc[vb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pk[kk], oacc[vb2], 0, 0, 0);
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+          oacc[s][vb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pk[s], oacc[s][vb], 0, 0, 0);
       }
     }
   };
 
-  // One pipeline step for tile kt (B = kt & 1): K tile kt+1 is in K buffer 1-B, V tile kt
-  // in V buffer B.  Start the direct loads of K tile kt+2 into K buffer B and V tile kt+1
-  // into V buffer 1-B (both last read in the previous step), run the tile, wait for the
-  // loads, barrier.  The loads are unconditional: past the last live tile they fetch
-  // zeros or unused keys into buffers nobody reads.
-  f32x16 sa[2], sb[2];
-  auto step = [&](auto bufc, int kt, f32x16 (&scur)[2], f32x16 (&snext)[2]) {
-    constexpr int B = decltype(bufc)::value;
-    load_k(bufc, kt + 2);
-    load_v(std::integral_constant<int, 1 - B>{}, kt + 1);
-    tile(std::integral_constant<int, 1 - B>{}, bufc, kt, scur, snext);
-    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's direct loads have landed
-    __syncthreads();
+  // One pipeline step for tile kt in buffer B = kt % 3: start the direct loads of tile kt+2
+  // into buffer (kt+2) % 3 (last read at tile kt-1, behind that tile's barrier), compute tile
+  // kt if any of this wave's rows sees it, wait for this wave's copies of tile kt+1 (issued a
+  // step ago; those of kt+2 stay in flight), barrier.  The loads are unconditional: past the
+  // block's end they fetch zeros into buffers nobody reads.
+  auto step = [&](auto bufc, auto bufn, int kt) {
+    load_kv(bufn, kt + 2);
+    if (kt < wt_live) tile(bufc, kt);
+    tile_barrier<LPW>();
   };
 
-  load_k(std::integral_constant<int, 0>{}, 0);
-  load_v(std::integral_constant<int, 0>{}, 0);
-  load_k(std::integral_constant<int, 1>{}, 1);
-  __builtin_amdgcn_s_waitcnt(0x0F70);
-  __syncthreads();
-  scores(std::integral_constant<int, 0>{}, sa);
-  // The first step's copy of K tile 2 goes into K buffer 0, which every wave has just read
-  // for tile 0's scores: no wave may start it before all of them are done.  (Later steps
-  // refill a buffer read in the step before, behind that step's barrier.)
-  __syncthreads();
-  for (int kt = 0; kt < kt_live; kt += 2) {
-    step(std::integral_constant<int, 0>{}, kt, sa, sb);
-    if (kt + 1 < kt_live) step(std::integral_constant<int, 1>{}, kt + 1, sb, sa);
+  load_kv(I0{}, 0);
+  load_kv(I1{}, 1);
+  tile_barrier<LPW>();   // tile 0 has landed; tile 1 may still be in flight
+  for (int kt = 0; kt < kt_live; kt += 3) {
+    step(I0{}, I2{}, kt);
+    if (kt + 1 < kt_live) step(I1{}, I0{}, kt + 1);
+    if (kt + 2 < kt_live) step(I2{}, I1{}, kt + 2);
   }
+  wait_vmcnt<0>();   // the last copies (past the live tiles) land before the LDS is released
 
   // ---- write the state back ----------------------------------------------------------
-  if (row_ok) {
-    if (hi == 0) {
-      p.m[srow] = l_run == 0.f ? -INFINITY : m_run;
-      p.l[srow] = l_run;
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    float la, lb;
+    pair32(l_run[s], la, lb);
+    const float l_row = la + lb;
+    if (row_ok[s]) {
+      if (hi == 0) {
+        p.m[srow[s]] = l_row == 0.f ? -INFINITY : m_run[s];
+        p.l[srow[s]] = l_row;
+      }
+      float* op = p.o_acc + srow[s] * D + 4 * hi;
+#pragma unroll
+      for (int vb = 0; vb < VB; ++vb)
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+          *reinterpret_cast<float4*>(op + vb * 32 + 8 * a) =
+              make_float4(oacc[s][vb][4 * a + 0], oacc[s][vb][4 * a + 1], oacc[s][vb][4 * a + 2],
+                          oacc[s][vb][4 * a + 3]);
     }
-    float* op = p.o_acc + srow * D + 4 * hi;
-#pragma unroll
-    for (int vb2 = 0; vb2 < VB; ++vb2)
-#pragma unroll
-      for (int a = 0; a < 4; ++a)
-        *reinterpret_cast<float4*>(op + vb2 * 32 + 8 * a) =
-            make_float4(oacc[vb2][4 * a + 0], oacc[vb2][4 * a + 1], oacc[vb2][4 * a + 2],
-                        oacc[vb2][4 * a + 3]);
   }
 
   if (DEBUG) {
