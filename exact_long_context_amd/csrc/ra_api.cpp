@@ -29,6 +29,11 @@ struct ra_state {
   int finalized;
   ra_stats stats;
   unsigned long long* dbg;
+  // bf16 blocks of at least kKeyNormMinKeys keys: bounds of the largest key norm per 32-key
+  // tile, computed by a short pass before the step kernel so that it can skip its per-score
+  // guard (device, owned by the state, grown on demand outside stream capture)
+  float* knorm;
+  size_t knorm_cap;   // floats
 };
 
 // The backward of one rank's lap: the resident Q_r and dO_r, the forward's lse_r, and the
@@ -135,6 +140,10 @@ int32_t pos_stride(int32_t mask_kind, const ra_desc* d) {
 // section "Striping the sequence to flatten the triangle": 2P chunks, rank r holds chunks
 // r and 2P-1-r) gives four, one per (query chunk, key chunk): each is a contiguous causal
 // block with its own diagonal, and a chunk pair wholly in the future is empty.
+// Blocks shorter than this take the step kernel's full guard: they are bound by the state's
+// HBM traffic, and the norm pass would add a launch for nothing.
+constexpr int32_t kKeyNormMinKeys = 4096;
+
 struct Sub {
   int32_t row0, rows, key0, keys, diag;
   int64_t pairs;   // allowed (row, key) pairs of one head
@@ -419,6 +428,39 @@ int ra_block_step(ra_state* st, const void* k, const void* v, int32_t kv_len, in
   }
   const size_t elem = d->dtype == RA_DTYPE_BF16 ? 2 : 4;
   hipStream_t stream = static_cast<hipStream_t>(d->stream);
+  // The key-tile norms of the whole block (tiles from its first key), when it is long enough
+  // for the step kernel's guard to matter.  A buffer that must grow while the stream is being
+  // captured is not grown: the launches then go without bounds (same result, full guard).
+  const int32_t n_tiles = (kv_len + ra::kBf16TileK - 1) / ra::kBf16TileK;
+  const float* knorm = nullptr;
+  if (d->dtype == RA_DTYPE_BF16 && kv_len >= kKeyNormMinKeys) {
+    const size_t need = (size_t)d->batch * d->kv_heads * n_tiles;
+    if (need > st->knorm_cap) {
+      hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+      hipError_t e = hipStreamIsCapturing(stream, &cs);
+      if (e != hipSuccess) return hip_fail(e, "hipStreamIsCapturing");
+      if (cs == hipStreamCaptureStatusNone) {
+        if (st->knorm) {
+          e = hipFree(st->knorm);
+          st->knorm = nullptr;
+          st->knorm_cap = 0;
+          if (e != hipSuccess) return hip_fail(e, "hipFree (key-tile norms)");
+        }
+        void* buf = nullptr;
+        e = hipMalloc(&buf, need * sizeof(float));
+        if (e != hipSuccess) return hip_fail(e, "hipMalloc (key-tile norms)");
+        st->knorm = static_cast<float*>(buf);
+        st->knorm_cap = need;
+      }
+    }
+    if (need <= st->knorm_cap) {
+      hipError_t e = ra::launch_key_tile_norms(k, d->kv_strides[0], d->kv_strides[1],
+                                               token_stride(d->kv_strides[2], kv_len, d->head_dim),
+                                               d->batch, d->kv_heads, kv_len, d->head_dim, st->knorm, stream);
+      if (e != hipSuccess) return hip_fail(e, "key-tile norm launch");
+      knorm = st->knorm;
+    }
+  }
   auto launch = [&](const Sub& b, int fresh) -> int {
     ra::StepParams p;
     p.q = static_cast<const char*>(st->q) + (int64_t)b.row0 * d->q_strides[2] * elem;
@@ -444,6 +486,9 @@ int ra_block_step(ra_state* st, const void* k, const void* v, int32_t kv_len, in
     p.scale_log2 = d->softmax_scale * 1.4426950408889634f;
     p.fresh = fresh;
     p.dbg = st->dbg;
+    // tiles of a sub-block line up with the block's when it starts on a tile boundary
+    p.knorm = knorm && b.key0 % ra::kBf16TileK == 0 ? knorm + b.key0 / ra::kBf16TileK : nullptr;
+    p.knorm_stride = n_tiles;
     hipError_t e = d->dtype == RA_DTYPE_BF16 ? ra::launch_step_bf16(p, d->head_dim, stream)
                                              : ra::launch_step_f32(p, d->head_dim, stream);
     if (e != hipSuccess) return hip_fail(e, "step kernel launch");
@@ -798,6 +843,8 @@ int ra_bwd_destroy(ra_bwd* st) {
 }
 
 int ra_state_destroy(ra_state* st) {
+  // hipFree waits for the device, so work still reading the norms ends first
+  if (st && st->knorm) hipFree(st->knorm);
   delete st;
   return RA_OK;
 }

@@ -26,8 +26,14 @@ struct StepParams {
   int32_t diag;        // key t is visible to row i iff t <= i + diag
   float scale_log2;    // softmax scale * log2(e)
   int32_t fresh;       // 1: the state has never been written; start from the empty state
-  unsigned long long* dbg;  // optional device counters [4]: unmasked tiles, masked tiles, pairs,
-                            // and (row, tile) events where a row holding keys moved its reference
+  unsigned long long* dbg;  // optional device counters [5]: unmasked tiles, masked tiles, pairs,
+                            // (row, tile) events where a row holding keys moved its reference,
+                            // and (wave, tile) events decided by the key-norm bound (bf16)
+  // optional (bf16 only): an upper bound of the largest key norm |k| of every 32-key tile of
+  // this launch's keys (tile t = keys 32t .. 32t+31 after p.k), [B * Hkv][knorm_stride]; null:
+  // no bound, every tile takes the per-score guard
+  const float* knorm;
+  int32_t knorm_stride;
 };
 
 struct FinalizeParams {
@@ -130,6 +136,11 @@ constexpr int kDecodeRows = 32;   // packed (query head, token) rows per wave of
 constexpr int kDecodeTileK = 32;
 
 hipError_t launch_step_bf16(const StepParams& p, int head_dim, hipStream_t stream);
+// Upper bounds of the largest key norm of every 32-key tile of a bf16 K block [B, Hkv, n_k, d]
+// (strides in elements, multiples of 8), written as out[(b * Hkv + h) * n_tiles + t] with
+// n_tiles = ceil(n_k / 32); keys past n_k count as zero.
+hipError_t launch_key_tile_norms(const void* k, int64_t k_sb, int64_t k_sh, int64_t k_st, int batch,
+                                 int kv_heads, int n_k, int head_dim, float* out, hipStream_t stream);
 hipError_t launch_step_f32(const StepParams& p, int head_dim, hipStream_t stream);
 hipError_t launch_finalize(const FinalizeParams& p, hipStream_t stream);
 hipError_t launch_merge(const MergeParams& p, hipStream_t stream);

@@ -106,6 +106,16 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, in
 // 32 (base 2) above it, so the guard sends the row to the slow path without a test of its
 // own, while masked keys (x = -inf) never trip it.
 constexpr float kNoRef = -1e30f;
+// Relative margin on the norms behind the tile bound: covers the fp32 rounding of |q|^2, |k|^2,
+// their square roots and the score products themselves (all far below 2^-9).
+constexpr float kNormMargin = 1.001953125f;   // 1 + 2^-9
+
+// Key-tile bounds are read through the constant address space, so that each tile's bound is one
+// scalar load: a vector load would count against vmcnt, and waiting for it would wait for the
+// tile copies in flight as well.  no_bound stands in when a launch has no bounds: its bits
+// (a NaN) exceed every threshold's as signed integers, so every tile takes the full guard.
+typedef __attribute__((address_space(4))) const unsigned const_u32;
+__constant__ unsigned no_bound[1] = {0x7fffffffu};
 
 // max(a, b, c) in one instruction (the compiler splits fmaxf chains into two-input maxima)
 __device__ __forceinline__ float max3(float a, float b, float c) {
@@ -157,7 +167,9 @@ void step_bf16_kernel(StepParams p) {
   // q fragment 0 of both sub-tiles of every wave, parked in LDS: read back once per tile,
   // it frees 8 registers that the tile's probabilities need
   __shared__ __attribute__((aligned(16))) unsigned char q_park[4 * 2 * 1024];
-  __shared__ unsigned long long dbg_acc[2];
+  // |q| * |c2| of every row (with a margin), read only when the wave's threshold is rebuilt
+  __shared__ float qn_park[4 * 2 * 64];
+  __shared__ unsigned long long dbg_acc[3];
   unsigned char* const k_tiles[3] = {k_t0, k_t1, k_t2};
   unsigned char* const v_tiles[3] = {v_t0, v_t1, v_t2};
 #define ktile(bufc) (k_tiles[decltype(bufc)::value])
@@ -197,7 +209,7 @@ void step_bf16_kernel(StepParams p) {
   const int wt_live = tiles_live(w0, w1, p.diag, p.n_k, BK);
   const int wt_full = tiles_full(w0, w1, p.diag, p.n_k, BK);
 
-  if (DEBUG && tid < 2) dbg_acc[tid] = 0;
+  if (DEBUG && tid < 3) dbg_acc[tid] = 0;
 
   // ---- staging: global -> LDS directly ------------------------------------------------
   const __bf16* kg = static_cast<const __bf16*>(p.k) + (int64_t)b * p.k_sb + (int64_t)kvh * p.k_sh;
@@ -256,9 +268,23 @@ void step_bf16_kernel(StepParams p) {
     }
   }
 
+  const float c2 = p.scale_log2;
 #pragma unroll
-  for (int s = 0; s < 2; ++s)
+  for (int s = 0; s < 2; ++s) {
     *reinterpret_cast<bf16x8*>(q_park + (wave * 2 + s) * 1024 + lane * 16) = qf[s][0];
+    // |q|^2 of the row: this lane's half of the dims, then the partner lane's
+    float ss = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        const bf16x2 x = {qf[s][ks][e], qf[s][ks][e + 1]};
+        ss = __builtin_amdgcn_fdot2_f32_bf16(x, x, ss, false);
+      }
+    float a, bb;
+    pair32(ss, a, bb);
+    qn_park[(wave * 2 + s) * 64 + lane] = __builtin_sqrtf(a + bb) * __builtin_fabsf(c2) * kNormMargin;
+  }
 
   f32x16 oacc[2][VB];
   // m_run: the row's finite reference (kNoRef before any key); l_run: this lane's share of
@@ -303,9 +329,35 @@ void step_bf16_kernel(StepParams p) {
   const int kb0 = hi * 512 + r32 * 16;
   const int vb0 = (4 * (lane >> 5) + ((lane >> 2) & 3)) * 64 + (16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * 2;
 
-  const float c2 = p.scale_log2;
   unsigned long long my_pairs = 0;
   unsigned my_moves = 0;   // reference moves of this lane's rows that already held keys
+  unsigned my_bounded = 0; // tiles of this wave whose key-norm bound made the scores' maximum moot
+
+  // The wave's threshold on the tile bound: T = min over its rows of (32 + m) / (|q| |c2|), so
+  // that a tile whose largest key norm is <= T has every score x with x c2 - m <= 32
+  // (Cauchy-Schwarz: |<q, k>| <= |q| |k|).  Returned as the bits of T, which order like T
+  // against any norm (>= 0) as signed integers, so the per-tile test is one scalar compare.
+  // Rebuilt only when a reference moves.
+  auto threshold_bits = [&]() -> int {
+    float t = INFINITY;
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const float qn = qn_park[(wave * 2 + s) * 64 + lane];
+      const float num = 32.f + m_run[s];
+      const float ts = qn > 0.f ? num / qn : (num >= 0.f ? INFINITY : -INFINITY);
+      t = fminf(t, ts);
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) t = fminf(t, __shfl_xor(t, off));
+    return __builtin_amdgcn_readfirstlane(__float_as_int(t));
+  };
+  int t_bits = threshold_bits();
+  // this launch's key-tile bounds for the workgroup's KV head
+  // Without bounds every tile reads the one entry of no_bound, which no threshold passes: a
+  // select instead of a branch around the load.
+  const_u32* knorm_row = p.knorm ? (const_u32*)(p.knorm + (int64_t)(b * p.kv_heads + kvh) * p.knorm_stride)
+                                 : (const_u32*)no_bound;
+  const int kn_step = p.knorm ? 1 : 0;
 
   // One 32-key tile from buffer B: S^T = K Q^T for both sub-tiles (each K fragment feeds
   // both), the guard on the reference, then per 16-key half the probabilities and
@@ -314,6 +366,8 @@ void step_bf16_kernel(StepParams p) {
   auto tile = [&](auto bufc, int kt) {
     const unsigned char* kt_base = ktile(bufc);
     const unsigned char* vt_base = vtile(bufc);
+    // the tile's key-norm bound, loaded first so that the scores hide its latency
+    const int kn_bits = (int)knorm_row[__builtin_amdgcn_readfirstlane(kt * kn_step)];
     f32x16 sacc[2];
     {
       // q fragment 0 comes back from LDS (a volatile read: the compiler may not keep it in a
@@ -351,43 +405,49 @@ void step_bf16_kernel(StepParams p) {
     }
 
     // The guard on the reference, once per tile and before any probability is formed: every
-    // term 2^(x - m_run) must stay <= 2^32 (fp32 and bf16 hold it without loss).  fma is
-    // monotonic in x, so it is enough that this lane's largest score passes; a row whose lane
-    // does not (or that has no reference yet: kNoRef makes any visible score fail) moves its
-    // reference to the row's maximum here, rescaling l and O~.  That is rare (in practice the
-    // first visible tile of a row), so the common path is one straight run of probabilities
-    // and value products with no branch.
-    float mx[2];
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      float a = max3(sacc[s][0], sacc[s][1], sacc[s][2]);
-#pragma unroll
-      for (int j = 3; j < 15; j += 2) a = max3(a, sacc[s][j], sacc[s][j + 1]);
-      mx[s] = fmaxf(a, sacc[s][15]);
-    }
-    const unsigned long long bad0 = __builtin_amdgcn_ballot_w64(__builtin_fmaf(mx[0], c2, -m_run[0]) > 32.f);
-    const unsigned long long bad1 = __builtin_amdgcn_ballot_w64(__builtin_fmaf(mx[1], c2, -m_run[1]) > 32.f);
-    if (bad0 | bad1) {
+    // term 2^(x - m_run) must stay <= 2^32 (fp32 and bf16 hold it without loss).  First the
+    // tile bound: if the tile's largest key norm is within the wave's threshold, every score
+    // passes and nothing is looked at (one scalar compare).  Otherwise each lane's largest score
+    // is checked (fma is monotonic in x, so the largest decides); a row whose lane fails (or
+    // that has no reference yet: kNoRef makes any visible score fail) moves its reference to
+    // the row's maximum here, rescaling l and O~.  That is rare (in practice the first visible
+    // tile of a row), so the common path is one straight run of probabilities and value
+    // products with no branch.
+    if (DEBUG && kn_bits <= t_bits && lane == 0) ++my_bounded;
+    if (kn_bits > t_bits) {
+      float mx[2];
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
-        const unsigned long long bad = s == 0 ? bad0 : bad1;
-        // the row is bad if either of its lanes is (lane r32 and lane r32 + 32)
-        const unsigned rows = (unsigned)bad | (unsigned)(bad >> 32);
-        const bool row_bad = (rows >> r32) & 1u;
-        float a, bb;
-        pair32(mx[s], a, bb);
-        const float mrow = fmaxf(a, bb);
-        // a bad row moves its reference to its maximum: l and O~ scale by 2^(m_old - m_new),
-        // which is 0 for a row that had no reference (its O~ and l are 0 as well)
-        const float m_new = row_bad ? mrow * c2 : m_run[s];
-        const float alpha = __builtin_amdgcn_exp2f(m_run[s] - m_new);
-        if (DEBUG && row_ok[s] && hi == 0 && row_bad && m_run[s] != kNoRef) ++my_moves;
-        l_run[s] *= alpha;
+        float a = max3(sacc[s][0], sacc[s][1], sacc[s][2]);
 #pragma unroll
-        for (int vb = 0; vb < VB; ++vb)
+        for (int j = 3; j < 15; j += 2) a = max3(a, sacc[s][j], sacc[s][j + 1]);
+        mx[s] = fmaxf(a, sacc[s][15]);
+      }
+      const unsigned long long bad0 = __builtin_amdgcn_ballot_w64(__builtin_fmaf(mx[0], c2, -m_run[0]) > 32.f);
+      const unsigned long long bad1 = __builtin_amdgcn_ballot_w64(__builtin_fmaf(mx[1], c2, -m_run[1]) > 32.f);
+      if (bad0 | bad1) {
 #pragma unroll
-          for (int j = 0; j < 16; ++j) oacc[s][vb][j] *= alpha;
-        m_run[s] = m_new;
+        for (int s = 0; s < 2; ++s) {
+          const unsigned long long bad = s == 0 ? bad0 : bad1;
+          // the row is bad if either of its lanes is (lane r32 and lane r32 + 32)
+          const unsigned rows = (unsigned)bad | (unsigned)(bad >> 32);
+          const bool row_bad = (rows >> r32) & 1u;
+          float a, bb;
+          pair32(mx[s], a, bb);
+          const float mrow = fmaxf(a, bb);
+          // a bad row moves its reference to its maximum: l and O~ scale by 2^(m_old - m_new),
+          // which is 0 for a row that had no reference (its O~ and l are 0 as well)
+          const float m_new = row_bad ? mrow * c2 : m_run[s];
+          const float alpha = __builtin_amdgcn_exp2f(m_run[s] - m_new);
+          if (DEBUG && row_ok[s] && hi == 0 && row_bad && m_run[s] != kNoRef) ++my_moves;
+          l_run[s] *= alpha;
+#pragma unroll
+          for (int vb = 0; vb < VB; ++vb)
+#pragma unroll
+            for (int j = 0; j < 16; ++j) oacc[s][vb][j] *= alpha;
+          m_run[s] = m_new;
+        }
+        t_bits = threshold_bits();
       }
     }
 
@@ -475,12 +535,14 @@ void step_bf16_kernel(StepParams p) {
   if (DEBUG) {
     if (my_pairs) atomicAdd(&dbg_acc[0], my_pairs);
     if (my_moves) atomicAdd(&dbg_acc[1], (unsigned long long)my_moves);
+    if (my_bounded) atomicAdd(&dbg_acc[2], (unsigned long long)my_bounded);
     __syncthreads();
     if (tid == 0) {
       atomicAdd(&p.dbg[0], (unsigned long long)kt_full);
       atomicAdd(&p.dbg[1], (unsigned long long)(kt_live - kt_full));
       atomicAdd(&p.dbg[2], dbg_acc[0]);
       atomicAdd(&p.dbg[3], dbg_acc[1]);
+      atomicAdd(&p.dbg[4], dbg_acc[2]);
     }
   }
 #undef ktile
@@ -499,7 +561,63 @@ hipError_t launch_d(const StepParams& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// Key-tile norms: one wave per (batch, KV head, 32-key tile).  Lanes 2j and 2j+1 take key j
+// of the tile, half of its dims each, in 16-byte loads; the tile's largest |k| (times the
+// margin) is written by lane 0.  Keys past the block's end contribute nothing.
+template <int D>
+__global__ __launch_bounds__(256) void key_tile_norm_kernel(const __bf16* k, int64_t k_sb, int64_t k_sh,
+                                                            int64_t k_st, int kv_heads, int n_k,
+                                                            int n_tiles, int64_t n_waves, float* out) {
+  const int64_t w = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (w >= n_waves) return;   // whole waves only
+  const int lane = threadIdx.x & 63;
+  const int t = (int)(w % n_tiles);
+  const int64_t bh = w / n_tiles;
+  const int64_t b = bh / kv_heads, h = bh % kv_heads;
+  const int key = t * BK + (lane >> 1);
+  float ss = 0.f;
+  if (key < n_k) {
+    const __bf16* row = k + b * k_sb + h * k_sh + (int64_t)key * k_st + (lane & 1) * (D / 2);
+#pragma unroll
+    for (int c = 0; c < D / 2; c += 8) {
+      const bf16x8 x = *reinterpret_cast<const bf16x8*>(row + c);
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        const bf16x2 y = {x[e], x[e + 1]};
+        ss = __builtin_amdgcn_fdot2_f32_bf16(y, y, ss, false);
+      }
+    }
+  }
+  ss += __shfl_xor(ss, 1);
+  float nrm = __builtin_sqrtf(ss);
+#pragma unroll
+  for (int off = 2; off < 64; off <<= 1) nrm = fmaxf(nrm, __shfl_xor(nrm, off));
+  if (lane == 0) out[bh * n_tiles + t] = nrm * kNormMargin;
+}
+
 }  // namespace
+
+hipError_t launch_key_tile_norms(const void* k, int64_t k_sb, int64_t k_sh, int64_t k_st, int batch,
+                                 int kv_heads, int n_k, int head_dim, float* out, hipStream_t stream) {
+  const int n_tiles = (n_k + BK - 1) / BK;
+  const int64_t n_waves = (int64_t)batch * kv_heads * n_tiles;
+  if (n_waves == 0) return hipSuccess;
+  const int64_t grid = (n_waves + 3) / 4;
+  if (grid > 0x7fffffff) return hipErrorInvalidValue;
+  const __bf16* kb = static_cast<const __bf16*>(k);
+  switch (head_dim) {
+    case 64:
+      hipLaunchKernelGGL(key_tile_norm_kernel<64>, dim3((unsigned)grid), dim3(256), 0, stream, kb, k_sb, k_sh,
+                         k_st, kv_heads, n_k, n_tiles, n_waves, out);
+      break;
+    case 128:
+      hipLaunchKernelGGL(key_tile_norm_kernel<128>, dim3((unsigned)grid), dim3(256), 0, stream, kb, k_sb, k_sh,
+                         k_st, kv_heads, n_k, n_tiles, n_waves, out);
+      break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
 
 hipError_t launch_step_bf16(const StepParams& p, int head_dim, hipStream_t stream) {
   switch (head_dim) {

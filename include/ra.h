@@ -159,7 +159,12 @@ int ra_state_resume(const ra_desc* desc, const void* q, void* workspace, ra_stat
  * offsets, and merge the result into the state.  A block with no allowed pair returns
  * RA_OK without launching (counted in blocks_skipped).  K_j and V_j are read by work
  * enqueued on desc.stream: the caller must not overwrite them until that work has
- * completed (record an event after this call). */
+ * completed (record an event after this call).  For bf16 blocks of at least 4096 keys a short
+ * pass first bounds the largest key norm of every 32-key tile (Cauchy-Schwarz then lets the
+ * step kernel skip its per-score guard on the reference): the state keeps those bounds in a
+ * device buffer of its own, 4 bytes per 32 keys per (batch, KV head), allocated on the first
+ * such call and grown when a longer block comes.  Under stream capture it is never grown; a
+ * block it does not fit is then stepped without bounds, with the same result. */
 int ra_block_step(ra_state* st, const void* k, const void* v, int32_t kv_len,
                   int32_t mask_kind, int64_t q_offset, int64_t k_offset);
 
@@ -170,19 +175,24 @@ int ra_block_step(ra_state* st, const void* k, const void* v, int32_t kv_len,
  * RA_E_STATE. */
 int ra_finalize(ra_state* st, float* o, float* lse);
 
-/* Release the host object (enqueues nothing; the workspace is the caller's). */
+/* Release the host object and the state's key-tile norm buffer, if ra_block_step made one
+ * (hipFree, which waits for the device first).  Enqueues nothing; the workspace is the
+ * caller's. */
 int ra_state_destroy(ra_state* st);
 
 /* Host-side counts accumulated by the planner over this state's steps. */
 int ra_get_stats(const ra_state* st, ra_stats* out);
 
-/* Debug: when counters is a device pointer to 4 zeroed uint64 values, every later
+/* Debug: when counters is a device pointer to 5 zeroed uint64 values, every later
  * ra_block_step of this state runs the counting variant of its kernel, which adds
  * (atomically, on the device) [0] the tiles it computed unmasked, [1] the tiles it computed
  * masked, [2] the allowed pairs it actually scored and [3] the (query row, key tile) events
  * in which a row that already held keys moved its reference m, rescaling l and O~ by
  * 2^(m_old - m_new) ("Ring attention" MCQ page, body: the running output is rescaled by
- * exp(old_max - new_max) when a new maximum appears).  ra_decode_step adds to [3] only.
+ * exp(old_max - new_max) when a new maximum appears), and [4] (bf16 only) the (wave of 64
+ * query rows, key tile) events in which the tile's key-norm bound showed every score within
+ * 2^32 of the reference, so that the scores' maximum was not taken.  ra_decode_step adds to
+ * [3] only.
  * NULL switches counting off. */
 int ra_state_set_debug_counters(ra_state* st, uint64_t* counters);
 

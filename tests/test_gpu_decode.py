@@ -312,7 +312,7 @@ def test_decode_live_rows_rescale_on_planted_sawtooth(case):
     outs = []
     for counted in (True, False):
         st = ra.RingState(qd, kd)
-        counters = torch.zeros(4, dtype=torch.int64, device="cuda")
+        counters = torch.zeros(5, dtype=torch.int64, device="cuda")
         if counted:
             st.set_debug_counters(counters)
         st.decode_step(kd, vd, NONE)

@@ -161,7 +161,7 @@ def test_mask_and_skip_decisions_bit_exact(dtype, mask):
     qd = q.cuda()
     for j in range(P):
         kp = oracle.tokens_of_rank(N, P, layout, j)
-        counters = torch.zeros(4, dtype=torch.int64, device="cuda")
+        counters = torch.zeros(5, dtype=torch.int64, device="cuda")
         st = ra.RingState(qd, kb[0], ring_size=P)
         st.set_debug_counters(counters)
         qo, ko = ra.block_offsets(mask, rank, j, n, n)
@@ -375,14 +375,14 @@ def _planted_lap_inputs(dtype, mask, rank, N, P, Hq, Hkv, order, seed):
     return q_pos, q, k, v
 
 
-def _assert_live_rescales_ran(q, kb, vb, rank, mask, P, order, dtype):
+def _assert_live_rescales_ran(q, kb, vb, rank, mask, P, order, dtype, bounded=None):
     """Run the lap twice, with and without the kernels' debug counters: the counting variant
     must report (row, tile) events in which a row holding keys moved its reference, and give
     bit for bit the product kernel's result.  The product run also checks, from the state
     after every step, that some rows holding keys raised m by more than 32 (base 2) in one
     step, which only the rescale path does."""
     import exact_long_context_amd as ra
-    counters = torch.zeros(4, dtype=torch.int64, device="cuda")
+    counters = torch.zeros(5, dtype=torch.int64, device="cuda")
     o_dbg, lse_dbg, _ = lap_with_steps(q, kb, vb, rank, mask, P, order=order, debug_counters=counters)
     n = q.shape[2]
     st = ra.RingState(q, kb[0], ring_size=P)
@@ -402,6 +402,9 @@ def _assert_live_rescales_ran(q, kb, vb, rank, mask, P, order, dtype):
     say(f"    live-row reference moves counted: {c[3]}; rows jumping > 32 between steps: {jumps}")
     assert c[3] > 0, "no row that held keys moved its reference: the rescale path did not run"
     assert jumps > 0
+    if bounded is not None:
+        say(f"    (wave, tile) events decided by the key-norm bound: {c[4]}")
+        assert (c[4] > 0) == bounded
     assert torch.equal(o, o_dbg) and torch.equal(lse, lse_dbg)
     return o, lse
 
@@ -445,6 +448,60 @@ def test_live_rows_rescale_on_planted_score_ladders(dtype, shuffled, mask, rank)
     assert np.max(np.abs(to64(lse)[fin] - ref_lse[fin])) <= tol
 
 
+@pytest.mark.parametrize("mask,rank", [(NONE, 3), (STRIPED, 6), (ZIGZAG, 2)])
+def test_key_norm_bound_with_planted_ladders(mask, rank):
+    """Blocks of 4096 keys, long enough for the key-norm bound on the reference (|x| <= |q| |k|,
+    checked once per tile in place of the scores' maximum).  On the planted ladders it holds
+    on the plateau blocks and fails where a block climbs, so both paths run in one lap: the
+    bound must decide some tiles, rows holding keys must still rescale, and the result must
+    match the oracle and the counting variant bit for bit."""
+    N, P, Hq, Hkv = 32768, 8, 4, 2
+    layout = LAYOUT[mask]
+    order = oracle.ring_visit_order(P, rank)
+    q_pos, q, k, v = _planted_lap_inputs("bf16", mask, rank, N, P, Hq, Hkv, order, 71 + rank + 7 * mask)
+    kb, vb = _blocks(k, v, P, layout)
+    say(f"  key-norm bound, planted ladders: mask={mask} rank={rank}, {P} blocks of {N // P} keys")
+    o, lse = _assert_live_rescales_ran(q.cuda(), kb, vb, rank, mask, P, order, "bf16", bounded=True)
+    ref, ref_lse = oracle.dense_attention(to64(q), to64(k), to64(v), q_pos, np.arange(N), mask != NONE)
+    assert_bf16_close(to64(o), ref, "O")
+    fin = np.isfinite(ref_lse)
+    assert np.max(np.abs(to64(lse)[fin] - ref_lse[fin])) <= 2e-2 * max(1.0, float(np.max(np.abs(ref_lse[fin]))))
+
+
+@pytest.mark.parametrize("case", ["loose", "ragged_zigzag"])
+def test_key_norm_bound_edges(case):
+    """Where the bound cannot help.  loose: queries and keys of scale 4 make |q| |k| far larger
+    than any score, so the bound never decides a tile and every tile takes the scores' maximum.
+    ragged_zigzag: chunks of 4100 keys, so the second key chunk of each block does not start
+    on a 32-key tile; its launches go without bounds while the first chunk's use them.  Both
+    must match the oracle."""
+    import exact_long_context_amd as ra
+    if case == "loose":
+        N, P, rank, mask, Hq, Hkv, vs = 32768, 8, 5, STRIPED, 4, 2, 4.0
+    else:
+        N, P, rank, mask, Hq, Hkv, vs = 16400, 2, 1, ZIGZAG, 4, 2, None
+    layout = LAYOUT[mask]
+    q_pos = oracle.tokens_of_rank(N, P, layout, rank)
+    kw = {} if vs is None else {"value_scale": vs}
+    q, k, _ = synth.random_case(83 + P, 1, Hq, Hkv, q_pos.size, N, 128, "bf16", **kw)
+    v = synth.random_case(84 + P, 1, Hq, Hkv, q_pos.size, N, 128, "bf16")[2]   # unit-scale outputs
+    kb, vb = _blocks(k, v, P, layout)
+    counters = torch.zeros(5, dtype=torch.int64, device="cuda")
+    say(f"  key-norm bound, {case}: {P} blocks of {kb[0].shape[2]} keys")
+    o, lse, _ = lap_with_steps(q.cuda(), kb, vb, rank, mask, P, debug_counters=counters)
+    torch.cuda.synchronize()
+    c = counters.cpu().tolist()
+    say(f"    (wave, tile) events decided by the bound: {c[4]}")
+    if case == "loose":
+        assert c[4] == 0
+    else:
+        assert c[4] > 0
+    ref, ref_lse = oracle.dense_attention(to64(q), to64(k), to64(v), q_pos, np.arange(N), True)
+    assert_bf16_close(to64(o), ref, "O")
+    fin = np.isfinite(ref_lse)
+    assert np.max(np.abs(to64(lse)[fin] - ref_lse[fin])) <= 2e-2 * max(1.0, float(np.max(np.abs(ref_lse[fin]))))
+
+
 def test_live_rows_rescale_after_resume():
     """Checkpoint after two blocks of a planted ladder, resume from a copy of the workspace
     and finish: the resumed launches load states that hold keys and must move their
@@ -462,7 +519,7 @@ def test_live_rows_rescale_after_resume():
         st.step(kb[j], vb[j], mask, *ra.block_offsets(mask, rank, j, n, n))
     saved = st.workspace.clone()
     st.close()
-    counters = torch.zeros(4, dtype=torch.int64, device="cuda")
+    counters = torch.zeros(5, dtype=torch.int64, device="cuda")
     st2 = ra.RingState(qd, kb[0], ring_size=P, workspace=saved, resume=True)
     st2.set_debug_counters(counters)
     for j in order[2:]:
