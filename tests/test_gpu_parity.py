@@ -240,15 +240,22 @@ def test_order_invariance_and_state_resume_bitwise():
     st3.close()
 
 
-def test_emulated_ring_lap_matches_steps_and_poison():
+@pytest.mark.parametrize("N", [4096, 32768], ids=["blocks512", "blocks4096"])
+def test_emulated_ring_lap_matches_steps_and_poison(N):
+    """The emulated lap equals the same blocks stepped one by one, bit for bit, with and
+    without poisoned receive buffers.  With blocks of 4096 keys the lap computes each received
+    block's key-norm bounds on its transfer stream, the steps inside ra_block_step."""
     import exact_long_context_amd as ra
-    N, P = 4096, 8
+    P = 8
     # contiguous ranks 0 and 2 skip seven and five blocks: their receive buffers are freed on
     # arrival, while the poison fill and the copies still run
-    for mask, rank in ((NONE, 3), (CONTIG, 6), (STRIPED, 5), (CONTIG, 0), (CONTIG, 2)):
+    cases = ((NONE, 3), (CONTIG, 6), (STRIPED, 5), (CONTIG, 0), (CONTIG, 2))
+    if N > 4096:
+        cases += ((ZIGZAG, 1),)
+    for mask, rank in cases:
         layout = LAYOUT[mask]
         q_pos = oracle.tokens_of_rank(N, P, layout, rank)
-        q, k, v = synth.random_case(17 + mask, 1, 4, 4, q_pos.size, N, 128, "bf16")
+        q, k, v = synth.random_case(17 + mask, 1, 4, 4 if N == 4096 else 2, q_pos.size, N, 128, "bf16")
         kb, vb = _blocks(k, v, P, layout)
         qd = q.cuda()
         o_steps, lse_steps, st_steps = lap_with_steps(qd, kb, vb, rank, mask, P)
