@@ -12,19 +12,17 @@
 //      S^T = K Q^T and dP^T = V dO^T (K and V rows from LDS as A, q and dO resident as B),
 //      dS^T formed in registers and rounded to bf16, then dQ^T += K^T dS^T with K^T read by
 //      ds_read_b64_tr_b16 from the same LDS tile: the forward's P V product with K for V.
-//  * bwd_kv_kernel (a workgroup of 4 waves owns the keys of one KV head: for dV 64 per wave as
-//      two halves, one wave per SIMD; for dK 32 per wave, two waves per SIMD, since it also
-//      holds V resident), in two modes launched one after the other: MODE_DV forms
-//      S = Q K^T and P, then dV^T += dO^T P; MODE_DK forms S and dP = dO V^T, then dS, then
-//      dK^T += Q^T dS (Q and dO rows from LDS as A, K and V resident as B, the transposed
-//      operands by ds_read_b64_tr_b16).  Each walks the query rows of every query head that
-//      reads its KV head.  Splitting dV from dK recomputes the scores once more but halves
-//      the streamed operand bytes per matrix instruction.
+//  * bwd_kv_kernel (a workgroup of 4 waves owns 128 keys of one KV head, 32 per wave, K
+//      resident in registers and V parked in LDS as B operands): per streamed tile of query
+//      rows it forms S = Q K^T and dP = dO V^T once, then P and dS in registers, and
+//      accumulates both dV^T += dO^T P and dK^T += Q^T dS (Q and dO rows from LDS as A, their
+//      transposes by ds_read_b64_tr_b16).  It walks the query rows of every query head that
+//      reads its KV head.
 // Streamed tiles are 32 or 64 rows, double-buffered, copied straight from HBM into LDS with
 // buffer_load ... lds; one XOR swizzle per tile keeps both the 16-byte operand reads and the
-// transposing reads free of bank conflicts.  Each output has one owner: no
-// atomics.  Only tiles holding an allowed pair are visited; the element mask runs on every
-// visited tile (cheap next to the five products).
+// transposing reads free of bank conflicts.  Each output has one owner: no atomics.  Only
+// tiles holding an allowed pair are visited, and the element mask runs only on tiles that
+// cross the causal diagonal.
 
 #include <hip/hip_runtime.h>
 
@@ -268,38 +266,34 @@ void bwd_dq_kernel(BwdParams p) {
 }
 
 // ------------------------------------------------------------------------------------------
-// Key-stationary kernels: a workgroup of 4 waves owns 128 * KH keys of one KV head, 32 * KH
-// per wave (with two halves each streamed operand read feeds both).
-// MODE_DV forms P and accumulates dV^T += dO^T P; MODE_DK forms P and dP, then dS, and
-// accumulates dK^T += Q^T dS.  Both recompute the scores; keeping them apart holds each one's
-// registers and LDS traffic per matrix instruction at the forward kernel's level.
-constexpr int MODE_DV = 0, MODE_DK = 1;
-// 32-key halves per wave.  Two halves (one wave per SIMD) halve the streamed operand bytes
-// per matrix instruction but leave one wave to hide every latency; measured, one half at two
-// waves per SIMD is faster for both modes (dV 10.4 ms -> see the design notes).
-template <int MODE>
-constexpr int kv_halves() { return 1; }
-// streamed tile rows of each kernel (32 or 64)
-constexpr int kBwdTileDq = 64, kBwdTileDv = 64, kBwdTileDk = 32;
+// Key-stationary kernel: a workgroup of 4 waves owns 128 keys of one KV head, 32 per wave, and
+// walks the query rows of every query head that reads that KV head.  Per streamed tile of 32
+// query rows it forms S = Q K^T and dP = dO V^T once, then P and dS in registers, and
+// accumulates both dV^T += dO^T P and dK^T += Q^T dS (the transposed Q and dO operands from
+// the same LDS tiles by ds_read_b64_tr_b16): 8 d flops per pair where separate dV and dK
+// passes took 10 d.  K stays in registers as the score product's B operand; V, the dP
+// product's B operand, is parked in LDS (one 1 KB fragment per wave and k-step, read back per
+// tile), which frees the registers the second accumulator needs at two waves per SIMD.
+constexpr int kBwdTileDq = 64, kBwdTileKv = 32;   // streamed tile rows of each kernel
 
-template <int D, int MODE, int BT>
-__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(3 - kv_halves<MODE>(), 3 - kv_halves<MODE>())))
+template <int D, int BT>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void bwd_kv_kernel(BwdParams p) {
-  constexpr int KH = kv_halves<MODE>();
-  constexpr int KW = 32 * KH;   // keys per wave
+  constexpr int KW = 32;        // keys per wave
   constexpr int KO = 4 * KW;    // keys per workgroup
   constexpr int NH = BT / 32;   // 32-row halves of a streamed tile
   using M = TileMap<D, BT>;
   constexpr int KS = M::KS, VB = M::VB, RB = M::RB;
-  constexpr bool DK = MODE == MODE_DK;
   __shared__ __attribute__((aligned(16))) unsigned char q_t0[BT * RB];
   __shared__ __attribute__((aligned(16))) unsigned char q_t1[BT * RB];
   __shared__ __attribute__((aligned(16))) unsigned char o_t0[BT * RB];
   __shared__ __attribute__((aligned(16))) unsigned char o_t1[BT * RB];
   __shared__ __attribute__((aligned(16))) float lse_t[2][BT];
   __shared__ __attribute__((aligned(16))) float d_t[2][BT];
+  __shared__ __attribute__((aligned(16))) unsigned char v_park[4 * KS * 1024];
   unsigned char* const q_tiles[2] = {q_t0, q_t1};
   unsigned char* const o_tiles[2] = {o_t0, o_t1};
+  typedef __attribute__((address_space(3))) const volatile bf16x8 lds_cvbf16x8;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -320,19 +314,17 @@ void bwd_kv_kernel(BwdParams p) {
   const int n_rt = (p.n_q - r_start + BT - 1) / BT;   // query tiles per head
   const int n_it = n_rt * p.group;                     // over every head of the group
 
-  int key[KH];
-  bool key_ok[KH];
-  bf16x8 kf[KH][KS], vf[KH][DK ? KS : 1];
-#pragma unroll
-  for (int kh = 0; kh < KH; ++kh) {
-    key[kh] = t0 + wave * KW + kh * 32 + r32;
-    key_ok[kh] = key[kh] < p.n_k;
-    const __bf16* krow = static_cast<const __bf16*>(p.k) + (int64_t)b * p.k_sb + (int64_t)g * p.k_sh + (int64_t)key[kh] * p.k_st + hi * 8;
-    const __bf16* vrow = static_cast<const __bf16*>(p.v) + (int64_t)b * p.k_sb + (int64_t)g * p.k_sh + (int64_t)key[kh] * p.k_st + hi * 8;
+  const int key = t0 + wave * KW + r32;
+  const bool key_ok = key < p.n_k;
+  bf16x8 kf[KS];
+  {
+    const int64_t row = (int64_t)b * p.k_sb + (int64_t)g * p.k_sh + (int64_t)key * p.k_st + hi * 8;
+    const __bf16* krow = static_cast<const __bf16*>(p.k) + row;
+    const __bf16* vrow = static_cast<const __bf16*>(p.v) + row;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      kf[kh][ks] = row_chunk(krow + ks * 16, key_ok[kh]);
-      if constexpr (DK) vf[kh][ks] = row_chunk(vrow + ks * 16, key_ok[kh]);
+      kf[ks] = row_chunk(krow + ks * 16, key_ok);
+      *reinterpret_cast<bf16x8*>(v_park + (wave * KS + ks) * 1024 + lane * 16) = row_chunk(vrow + ks * 16, key_ok);
     }
   }
   const float c2 = p.scale * kLog2e;
@@ -340,13 +332,14 @@ void bwd_kv_kernel(BwdParams p) {
   const int row_bytes = (int)(p.q_st * 2);
   map.init(lane, wave, row_bytes);
 
-  f32x16 acc[KH][VB];
+  f32x16 acck[VB], accv[VB];   // dK^T and dV^T of the wave's 32 keys
 #pragma unroll
-  for (int kh = 0; kh < KH; ++kh)
+  for (int vb = 0; vb < VB; ++vb)
 #pragma unroll
-    for (int vb = 0; vb < VB; ++vb)
-#pragma unroll
-      for (int j = 0; j < 16; ++j) acc[kh][vb][j] = 0.f;
+    for (int j = 0; j < 16; ++j) {
+      acck[vb][j] = 0.f;
+      accv[vb][j] = 0.f;
+    }
 
   // iteration u: head g*group + u / n_rt, query rows r_start + (u % n_rt) * BT ..
   auto stage = [&](int buf, int u) {
@@ -364,7 +357,7 @@ void bwd_kv_kernel(BwdParams p) {
       // +inf for a row outside the launch or one that saw no key in the forward: 2^(x - lse) = 0
       const float l2 = ok ? p.lse[sr] * kLog2e : INFINITY;
       lse_t[buf][tid] = l2 == -INFINITY ? INFINITY : l2;
-      if constexpr (DK) d_t[buf][tid] = ok ? p.D[sr] : 0.f;
+      d_t[buf][tid] = ok ? p.D[sr] : 0.f;
     }
   };
 
@@ -374,75 +367,56 @@ void bwd_kv_kernel(BwdParams p) {
     const int r0 = r_start + (u % n_rt) * BT;
     const unsigned char* qt_b = q_tiles[B];
     const unsigned char* ot_b = o_tiles[B];
-    f32x16 s[KH][NH], dp[KH][DK ? NH : 1];
+    f32x16 s[NH], dp[NH];
 #pragma unroll
-    for (int kh = 0; kh < KH; ++kh)
+    for (int rh = 0; rh < NH; ++rh)
 #pragma unroll
-      for (int rh = 0; rh < NH; ++rh)
+      for (int j = 0; j < 16; ++j) {
+        s[rh][j] = 0.f;
+        dp[rh][j] = 0.f;
+      }
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          s[kh][rh][j] = 0.f;
-          if constexpr (DK) dp[kh][rh][j] = 0.f;
-        }
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
+    for (int ks = 0; ks < KS; ++ks) {
+      const bf16x8 vb8 = *(lds_cvbf16x8*)(v_park + (wave * KS + ks) * 1024 + lane * 16);
 #pragma unroll
       for (int rh = 0; rh < NH; ++rh) {
-        const bf16x8 qa = map.rd(qt_b, ks, rh);
-#pragma unroll
-        for (int kh = 0; kh < KH; ++kh) s[kh][rh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[kh][ks], s[kh][rh], 0, 0, 0);
-        if constexpr (DK) {
-          const bf16x8 oa = map.rd(ot_b, ks, rh);
-#pragma unroll
-          for (int kh = 0; kh < KH; ++kh) dp[kh][rh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa, vf[kh][ks], dp[kh][rh], 0, 0, 0);
-        }
+        s[rh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(map.rd(qt_b, ks, rh), kf[ks], s[rh], 0, 0, 0);
+        dp[rh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(map.rd(ot_b, ks, rh), vb8, dp[rh], 0, 0, 0);
       }
-    // lane holds key key[kh] against tile rows 32*rh + 8*(j/4) + 4*hi + (j%4); a tile whose
+    }
+    // lane holds key `key` against tile rows 32*rh + 8*(j/4) + 4*hi + (j%4); a tile whose
     // first row sees the wave's last key needs no element mask
     const bool full = t0 + wave * KW + KW - 1 <= r0 + p.diag;
     const float4* lse4 = reinterpret_cast<const float4*>(&lse_t[B][0]);
     const float4* d4 = reinterpret_cast<const float4*>(&d_t[B][0]);
-    bf16x8 wb[KH][2 * NH];   // P (MODE_DV) or dS (MODE_DK) in bf16, per key half and 16-row step
+    bf16x8 wp[2 * NH], ws[2 * NH];   // P and dS in bf16, per 16-row step
 #pragma unroll
     for (int rh = 0; rh < NH; ++rh)
 #pragma unroll
       for (int a = 0; a < 4; ++a) {
         const float4 l4 = lse4[8 * rh + 2 * a + hi];   // rows 32rh + 8a + 4hi .. +3
         const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
-        float dvv[4] = {0.f, 0.f, 0.f, 0.f};
-        if constexpr (DK) {
-          const float4 dd = d4[8 * rh + 2 * a + hi];
-          dvv[0] = dd.x;
-          dvv[1] = dd.y;
-          dvv[2] = dd.z;
-          dvv[3] = dd.w;
-        }
+        const float4 dd = d4[8 * rh + 2 * a + hi];
+        const float dvv[4] = {dd.x, dd.y, dd.z, dd.w};
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
           const int j = 4 * a + c;
           const int i = r0 + 32 * rh + 8 * a + 4 * hi + c;
-#pragma unroll
-          for (int kh = 0; kh < KH; ++kh) {
-            // rows past the launch carry lse = +inf (p = 0) and keys past the block only feed
-            // their own, unstored, column: only the causal diagonal needs the element mask
-            const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kh][rh][j], c2, -lv[c]));
-            const float pr = (full || key[kh] <= i + p.diag) ? e : 0.f;
-            if constexpr (DK)
-              wb[kh][2 * rh + (j >> 3)][j & 7] = (__bf16)(pr * (dp[kh][rh][j] - dvv[c]) * p.scale);
-            else
-              wb[kh][2 * rh + (j >> 3)][j & 7] = (__bf16)pr;
-          }
+          // rows past the launch carry lse = +inf (p = 0) and keys past the block only feed
+          // their own, unstored, column: only the causal diagonal needs the element mask
+          const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s[rh][j], c2, -lv[c]));
+          const float pr = (full || key <= i + p.diag) ? e : 0.f;
+          ws[2 * rh + (j >> 3)][j & 7] = (__bf16)(pr * (dp[rh][j] - dvv[c]) * p.scale);
+          wp[2 * rh + (j >> 3)][j & 7] = (__bf16)pr;
         }
       }
-    const unsigned char* tr_tile = DK ? qt_b : ot_b;   // dK: Q^T dS; dV: dO^T P
+    // dV^T += dO^T P; dK^T += Q^T dS
 #pragma unroll
     for (int kk = 0; kk < 2 * NH; ++kk)
 #pragma unroll
       for (int vb = 0; vb < VB; ++vb) {
-        const bf16x8 ta = map.rd_t(tr_tile, kk, vb);
-#pragma unroll
-        for (int kh = 0; kh < KH; ++kh)
-          acc[kh][vb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta, wb[kh][kk], acc[kh][vb], 0, 0, 0);
+        accv[vb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(map.rd_t(ot_b, kk, vb), wp[kk], accv[vb], 0, 0, 0);
+        acck[vb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(map.rd_t(qt_b, kk, vb), ws[kk], acck[vb], 0, 0, 0);
       }
     __builtin_amdgcn_s_waitcnt(0x0F70);
     __syncthreads();
@@ -456,34 +430,34 @@ void bwd_kv_kernel(BwdParams p) {
     if (u + 1 < n_it) step(ic<1>{}, u + 1);
   }
 
-  float* const out = DK ? p.dk : p.dv;
+  // dK and dV of the wave's keys, added to the travelling block's accumulators
+  if (key_ok) {
+    const int64_t kbase = (((int64_t)b * p.kv_heads + g) * p.dkv_rows + key) * D + 4 * hi;
+    auto add = [&](float* out, const f32x16* acc) {
 #pragma unroll
-  for (int kh = 0; kh < KH; ++kh) {
-    if (!key_ok[kh]) continue;
-    const int64_t kbase = (((int64_t)b * p.kv_heads + g) * p.dkv_rows + key[kh]) * D + 4 * hi;
+      for (int vb = 0; vb < VB; ++vb)
 #pragma unroll
-    for (int vb = 0; vb < VB; ++vb)
-#pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        float4* o4 = reinterpret_cast<float4*>(out + kbase + vb * 32 + 8 * a);
-        float4 x = *o4;
-        x.x += acc[kh][vb][4 * a + 0];
-        x.y += acc[kh][vb][4 * a + 1];
-        x.z += acc[kh][vb][4 * a + 2];
-        x.w += acc[kh][vb][4 * a + 3];
-        *o4 = x;
-      }
+        for (int a = 0; a < 4; ++a) {
+          float4* o4 = reinterpret_cast<float4*>(out + kbase + vb * 32 + 8 * a);
+          float4 x = *o4;
+          x.x += acc[vb][4 * a + 0];
+          x.y += acc[vb][4 * a + 1];
+          x.z += acc[vb][4 * a + 2];
+          x.w += acc[vb][4 * a + 3];
+          *o4 = x;
+        }
+    };
+    add(p.dk, acck);
+    add(p.dv, accv);
   }
 }
 
 template <int D>
 hipError_t launch_d(const BwdParams& p, hipStream_t stream) {
   const int64_t gq = (int64_t)((p.n_q + BO - 1) / BO) * p.q_heads * p.batch;
-  const int64_t gv = (int64_t)((p.n_k + 128 * kv_halves<MODE_DV>() - 1) / (128 * kv_halves<MODE_DV>())) * p.kv_heads * p.batch;
-  const int64_t gk = (int64_t)((p.n_k + 128 * kv_halves<MODE_DK>() - 1) / (128 * kv_halves<MODE_DK>())) * p.kv_heads * p.batch;
+  const int64_t gkv = (int64_t)((p.n_k + 127) / 128) * p.kv_heads * p.batch;
   if (gq > 0) hipLaunchKernelGGL((bwd_dq_kernel<D, kBwdTileDq>), dim3((unsigned)gq), dim3(NT), 0, stream, p);
-  if (gv > 0) hipLaunchKernelGGL((bwd_kv_kernel<D, MODE_DV, kBwdTileDv>), dim3((unsigned)gv), dim3(NT), 0, stream, p);
-  if (gk > 0) hipLaunchKernelGGL((bwd_kv_kernel<D, MODE_DK, kBwdTileDk>), dim3((unsigned)gk), dim3(NT), 0, stream, p);
+  if (gkv > 0) hipLaunchKernelGGL((bwd_kv_kernel<D, kBwdTileKv>), dim3((unsigned)gkv), dim3(NT), 0, stream, p);
   return hipGetLastError();
 }
 
