@@ -475,23 +475,27 @@ def test_key_norm_bound_with_planted_ladders(mask, rank):
     assert np.max(np.abs(to64(lse)[fin] - ref_lse[fin])) <= 2e-2 * max(1.0, float(np.max(np.abs(ref_lse[fin]))))
 
 
-@pytest.mark.parametrize("case", ["loose", "ragged_zigzag"])
+@pytest.mark.parametrize("case", ["loose", "ragged_zigzag", "d64"])
 def test_key_norm_bound_edges(case):
     """Where the bound cannot help.  loose: queries and keys of scale 4 make |q| |k| far larger
     than any score, so the bound never decides a tile and every tile takes the scores' maximum.
     ragged_zigzag: chunks of 4100 keys, so the second key chunk of each block does not start
-    on a 32-key tile; its launches go without bounds while the first chunk's use them.  Both
+    on a 32-key tile; its launches go without bounds while the first chunk's use them.  d64:
+    head dimension 64 (the other instantiation of the norm pass and of the step kernel).  All
     must match the oracle."""
     import exact_long_context_amd as ra
+    d = 128
     if case == "loose":
         N, P, rank, mask, Hq, Hkv, vs = 32768, 8, 5, STRIPED, 4, 2, 4.0
+    elif case == "d64":
+        N, P, rank, mask, Hq, Hkv, vs, d = 32768, 8, 3, STRIPED, 4, 2, None, 64
     else:
         N, P, rank, mask, Hq, Hkv, vs = 16400, 2, 1, ZIGZAG, 4, 2, None
     layout = LAYOUT[mask]
     q_pos = oracle.tokens_of_rank(N, P, layout, rank)
     kw = {} if vs is None else {"value_scale": vs}
-    q, k, _ = synth.random_case(83 + P, 1, Hq, Hkv, q_pos.size, N, 128, "bf16", **kw)
-    v = synth.random_case(84 + P, 1, Hq, Hkv, q_pos.size, N, 128, "bf16")[2]   # unit-scale outputs
+    q, k, _ = synth.random_case(83 + P, 1, Hq, Hkv, q_pos.size, N, d, "bf16", **kw)
+    v = synth.random_case(84 + P, 1, Hq, Hkv, q_pos.size, N, d, "bf16")[2]   # unit-scale outputs
     kb, vb = _blocks(k, v, P, layout)
     counters = torch.zeros(5, dtype=torch.int64, device="cuda")
     say(f"  key-norm bound, {case}: {P} blocks of {kb[0].shape[2]} keys")
