@@ -55,6 +55,8 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int BQ = kBf16TileQ;  // 256 query rows per workgroup
 constexpr int BK = kBf16TileK;  // 32 keys per tile
@@ -116,12 +118,21 @@ constexpr float kNormMargin = 1.001953125f;   // 1 + 2^-9
 // (a NaN) exceed every threshold's as signed integers, so every tile takes the full guard.
 typedef __attribute__((address_space(4))) const unsigned const_u32;
 __constant__ unsigned no_bound[1] = {0x7fffffffu};
+// The stored maximum of a row that has seen no key: what a fresh state's rows read.
+__constant__ float no_key_m[1] = {-INFINITY};
 
 // max(a, b, c) in one instruction (the compiler splits fmaxf chains into two-input maxima)
 __device__ __forceinline__ float max3(float a, float b, float c) {
   float r;
   asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
   return r;
+}
+
+// x, through an empty asm statement the compiler cannot see into: what is computed from the
+// result starts here, not earlier
+__device__ __forceinline__ int opaque_copy(int x) {
+  asm volatile("" : "+v"(x));
+  return x;
 }
 
 // s_waitcnt with vmcnt = N (six bits: [3:0] and [15:14]); expcnt and lgkmcnt not waited on
@@ -243,6 +254,9 @@ void step_bf16_kernel(StepParams p) {
   };
 
   // ---- resident operands and state ---------------------------------------------------
+  // Every load the workgroup needs before its first tile is issued at once, with no branch
+  // between them, so that their latencies overlap: tile 0's copies, q, the state rows, then
+  // tile 1's copies.  Rows past the end read as zeros or are set aside below.
   int qrow[2];
   bool row_ok[2];
   int64_t srow[2];
@@ -252,25 +266,61 @@ void step_bf16_kernel(StepParams p) {
     row_ok[s] = qrow[s] < p.n_q;
     srow[s] = ((int64_t)b * p.q_heads + h) * p.state_rows + qrow[s];
   }
+  load_kv(I0{}, 0);
   bf16x8 qf[2][KS];
 #pragma unroll
   for (int s = 0; s < 2; ++s) {
-    const __bf16* qp = static_cast<const __bf16*>(p.q) + (int64_t)b * p.q_sb +
-                       (int64_t)h * p.q_sh + (int64_t)qrow[s] * p.q_st + hi * 8;
+    // a row past the end reads the last row (always there) and is zeroed below
+    const __bf16* qp = static_cast<const __bf16*>(p.q) + (int64_t)b * p.q_sb + (int64_t)h * p.q_sh +
+                       (int64_t)min(qrow[s], p.n_q - 1) * p.q_st + hi * 8;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      if (row_ok[s]) {
-        qf[s][ks] = *reinterpret_cast<const bf16x8*>(qp + ks * 16);
-      } else {
+    for (int ks = 0; ks < KS; ++ks) qf[s][ks] = *reinterpret_cast<const bf16x8*>(qp + ks * 16);
+  }
+  // The state rows of the workgroup through buffer resources over [i0, i1): rows past the
+  // end, and every row of a fresh state (a resource of no bytes), read as zeros.
+  f32x16 oacc[2][VB];
+  // m_run: the row's finite reference (kNoRef before any key); l_run: this lane's share of
+  // the row sum (its own keys' terms), the two lanes of a row added at the end
+  float m_run[2], l_run[2];
+  {
+    const int64_t srow0 = ((int64_t)b * p.q_heads + h) * p.state_rows + i0;
+    const int n_state = p.fresh ? 0 : i1 - i0;
+    const __amdgpu_buffer_rsrc_t ro = make_rsrc(p.o_acc + srow0 * D, (int64_t)n_state * D * 4);
+    // a fresh state's rows all read the one stored -inf (no key seen): a select of address
+    // and offset rather than a branch, which would hold the loads after it back
+    const __amdgpu_buffer_rsrc_t rm =
+        n_state ? make_rsrc(p.m + srow0, (int64_t)n_state * 4) : make_rsrc(no_key_m, 4);
+    const __amdgpu_buffer_rsrc_t rl = make_rsrc(p.l + srow0, (int64_t)n_state * 4);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) qf[s][ks][e] = (__bf16)0.0f;
-      }
+    for (int s = 0; s < 2; ++s) {
+      const int r = qrow[s] - i0;
+      const float m0 = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rm, n_state ? r * 4 : 0, 0, 0));
+      const float l0 = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rl, r * 4, 0, 0));
+      // a row that has seen no key (m = -inf), or is past the end, starts with no reference
+      m_run[s] = (!row_ok[s] || m0 == -INFINITY) ? kNoRef : m0;
+      l_run[s] = hi == 0 ? l0 : 0.f;
+#pragma unroll
+      for (int vb = 0; vb < VB; ++vb)
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          const f32x4 x = __builtin_bit_cast(
+              f32x4, __builtin_amdgcn_raw_buffer_load_b128(ro, (r * D + vb * 32 + 8 * a + 4 * hi) * 4, 0, 0));
+#pragma unroll
+          for (int e = 0; e < 4; ++e) oacc[s][vb][4 * a + e] = x[e];
+        }
     }
   }
+  load_kv(I1{}, 1);
 
   const float c2 = p.scale_log2;
 #pragma unroll
   for (int s = 0; s < 2; ++s) {
+    if (!row_ok[s]) {
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qf[s][ks][e] = (__bf16)0.0f;
+    }
     *reinterpret_cast<bf16x8*>(q_park + (wave * 2 + s) * 1024 + lane * 16) = qf[s][0];
     // |q|^2 of the row: this lane's half of the dims, then the partner lane's
     float ss = 0.f;
@@ -284,37 +334,6 @@ void step_bf16_kernel(StepParams p) {
     float a, bb;
     pair32(ss, a, bb);
     qn_park[(wave * 2 + s) * 64 + lane] = __builtin_sqrtf(a + bb) * __builtin_fabsf(c2) * kNormMargin;
-  }
-
-  f32x16 oacc[2][VB];
-  // m_run: the row's finite reference (kNoRef before any key); l_run: this lane's share of
-  // the row sum (its own keys' terms), the two lanes of a row added at the end
-  float m_run[2], l_run[2];
-#pragma unroll
-  for (int s = 0; s < 2; ++s) {
-    if (p.fresh || !row_ok[s]) {
-      m_run[s] = kNoRef;
-      l_run[s] = 0.f;
-#pragma unroll
-      for (int vb = 0; vb < VB; ++vb)
-#pragma unroll
-        for (int j = 0; j < 16; ++j) oacc[s][vb][j] = 0.f;
-    } else {
-      m_run[s] = p.m[srow[s]];
-      l_run[s] = hi == 0 ? p.l[srow[s]] : 0.f;
-      if (m_run[s] == -INFINITY) m_run[s] = kNoRef;
-      const float* op = p.o_acc + srow[s] * D + 4 * hi;
-#pragma unroll
-      for (int vb = 0; vb < VB; ++vb)
-#pragma unroll
-        for (int a = 0; a < 4; ++a) {
-          const float4 x = *reinterpret_cast<const float4*>(op + vb * 32 + 8 * a);
-          oacc[s][vb][4 * a + 0] = x.x;
-          oacc[s][vb][4 * a + 1] = x.y;
-          oacc[s][vb][4 * a + 2] = x.z;
-          oacc[s][vb][4 * a + 3] = x.w;
-        }
-    }
   }
 
   // Operand reads: one per-lane base per tensor, everything else immediate.
@@ -500,35 +519,62 @@ void step_bf16_kernel(StepParams p) {
     tile_barrier<LPW>();
   };
 
-  load_kv(I0{}, 0);
-  load_kv(I1{}, 1);
-  tile_barrier<LPW>();   // tile 0 has landed; tile 1 may still be in flight
+  tile_barrier<LPW>();   // tile 0 and the state have landed; tile 1 may still be in flight
   for (int kt = 0; kt < kt_live; kt += 3) {
     step(I0{}, I2{}, kt);
     if (kt + 1 < kt_live) step(I1{}, I0{}, kt + 1);
     if (kt + 2 < kt_live) step(I2{}, I1{}, kt + 2);
   }
-  wait_vmcnt<0>();   // the last copies (past the live tiles) land before the LDS is released
-
   // ---- write the state back ----------------------------------------------------------
+  // Every wave's copies have landed (the last ones, past the live tiles, fill buffers nobody
+  // reads) and its tile reads are done: the tile buffers are free.  O~ goes out through them,
+  // one 32-wide value block of a sub-tile at a time, so that each store instruction writes 8
+  // rows x 128 contiguous bytes rather than 32 bytes of each of 32 rows.  Wave w stages in its
+  // own tile buffer, in 4 KB regions (two used in turn where the buffer holds 8 KB, d = 128;
+  // one at d = 64, where the wave's LDS order alone keeps a block's reads ahead of the next
+  // block's writes): row R (0..31) of the block at R * 128, its
+  // 16-byte chunk C at slot C ^ ((R >> 1) & 7).  With that swizzle neither the writes in the
+  // accumulator layout (16 lanes: 16 rows, one chunk) nor the row-major reads (16 lanes: 2
+  // rows, 8 chunks) meet a bank twice.
+  __syncthreads();
+  unsigned char* const stage = wave == 0 ? k_t0 : wave == 1 ? k_t1 : wave == 2 ? k_t2 : v_t0;
+  // the staging addresses from a copy of the lane index made here, so that nothing of them is
+  // computed before the loop and held through it
+  const int el = opaque_copy(lane);
+  const int e32 = el & 31, ehi = el >> 5;
 #pragma unroll
   for (int s = 0; s < 2; ++s) {
     float la, lb;
     pair32(l_run[s], la, lb);
     const float l_row = la + lb;
-    if (row_ok[s]) {
-      if (hi == 0) {
-        p.m[srow[s]] = l_row == 0.f ? -INFINITY : m_run[s];
-        p.l[srow[s]] = l_row;
+    if (row_ok[s] && hi == 0) {
+      p.m[srow[s]] = l_row == 0.f ? -INFINITY : m_run[s];
+      p.l[srow[s]] = l_row;
+    }
+    // the sub-tile's rows through a resource that ends at the last row: stores past it are dropped
+    const __amdgpu_buffer_rsrc_t rs =
+        make_rsrc(p.o_acc + (((int64_t)b * p.q_heads + h) * p.state_rows + w0 + 32 * s) * D,
+                  (int64_t)max(0, p.n_q - w0 - 32 * s) * D * 4);
+#pragma unroll
+    for (int vb = 0; vb < VB; ++vb) {
+      static_assert(TB == 4096 || TB == 8192, "staging regions of 4 KB");
+      unsigned char* const half = stage + (TB == 8192 ? ((s * VB + vb) & 1) * 4096 : 0);
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+        *reinterpret_cast<f32x4*>(half + e32 * 128 + (((2 * a + ehi) ^ ((e32 >> 1) & 7)) * 16)) =
+            f32x4{oacc[s][vb][4 * a + 0], oacc[s][vb][4 * a + 1], oacc[s][vb][4 * a + 2], oacc[s][vb][4 * a + 3]};
+      f32x4 x[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int R = 8 * j + (el >> 3), C = el & 7;
+        x[j] = *reinterpret_cast<const f32x4*>(half + R * 128 + ((C ^ ((R >> 1) & 7)) * 16));
       }
-      float* op = p.o_acc + srow[s] * D + 4 * hi;
 #pragma unroll
-      for (int vb = 0; vb < VB; ++vb)
-#pragma unroll
-        for (int a = 0; a < 4; ++a)
-          *reinterpret_cast<float4*>(op + vb * 32 + 8 * a) =
-              make_float4(oacc[s][vb][4 * a + 0], oacc[s][vb][4 * a + 1], oacc[s][vb][4 * a + 2],
-                          oacc[s][vb][4 * a + 3]);
+      for (int j = 0; j < 4; ++j) {
+        const int R = 8 * j + (el >> 3), C = el & 7;
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, x[j]), rs,
+                                               (R * D + vb * 32 + C * 4) * 4, 0, 0);
+      }
     }
   }
 

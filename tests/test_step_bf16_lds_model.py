@@ -1,4 +1,4 @@
-"""A CPU model of the bf16 step kernel's use of LDS, in two parts.
+"""A CPU model of the bf16 step kernel's use of LDS, in three parts.
 
 Layouts: the kernel's direct copies (buffer_load ... lds: lane i of one instruction writes
 16 bytes at [16 i, 16 i + 16) after the instruction's LDS base, from the global offset it
@@ -11,7 +11,10 @@ Schedule: which buffer every wave's copies write and reads read, tile by tile, w
 may still be in flight (the barrier after tile t waits until all but the newest LPW copy
 instructions of the wave have landed), and whether any copy can overlap a read of, or another
 copy into, the same bytes.  The kernel's schedule (three buffers per tensor, copies two tiles
-ahead, vmcnt(LPW) at each barrier) has no such overlap; two buffers, or a looser wait, do."""
+ahead, vmcnt(LPW) at each barrier) has no such overlap; two buffers, or a looser wait, do.
+
+Epilogue: the accumulators leave through the tile buffers, each wave in its own, written in
+the accumulator layout and read back row-major; the model replays it element by element."""
 
 import itertools
 
@@ -232,3 +235,72 @@ def test_two_buffers_race():
 def test_a_looser_wait_races():
     # with vmcnt(2 LPW) the copies of tile t + 1 may still land while it is read
     assert any(h[0] == "read" and h[1] == h[2] for h in hazards(4, wait_n=8))
+
+
+# ---- the epilogue: O~ out through the tile buffers -------------------------------------------
+# After the loop every wave waits for all its copies and the workgroup meets at a barrier; then
+# wave w stages its accumulators through tile buffer w (K buffers 0-2, V buffer 0), one 32-wide
+# value block of a 32-row sub-tile at a time, in 4 KB regions: written in the accumulator layout
+# (lane (r, hi) holds row r, columns 8a + 4hi .. +3 of the block for a = 0..3), read back
+# row-major (lane l: row 8j + l // 8, 16-byte chunk l % 8, j = 0..3) and stored.  Row R of a
+# region sits at R * 128 with chunk C at slot C ^ ((R >> 1) & 7).
+
+def stage_base(D, s, vb):
+    """Offset of the region of (sub-tile s, value block vb) in the wave's tile buffer: two
+    regions used in turn where the buffer holds 8 KB (d = 128), one at d = 64 (4 KB)."""
+    return ((s * (D // 32) + vb) & 1) * 4096 if BK * 2 * D == 8192 else 0
+
+
+def acc_write(lane, a):
+    r, hi = lane & 31, lane >> 5
+    return r * 128 + (((2 * a + hi) ^ ((r >> 1) & 7)) * 16), r, 8 * a + 4 * hi
+
+
+def row_read(lane, j):
+    R, C = 8 * j + (lane >> 3), lane & 7
+    return R * 128 + ((C ^ ((R >> 1) & 7)) * 16), R, 4 * C
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_epilogue_staging_round_trip(D):
+    """Every accumulator element reaches its row and column, and no region leaves the wave's
+    tile buffer (the neighbouring buffers are other waves' staging areas)."""
+    TB = BK * 2 * D
+    lds = np.full(TB // 4, np.nan)
+    out = np.full((64, D), np.nan)
+    tag = lambda row, col: row * 1000.0 + col
+    for s in range(2):
+        for vb in range(D // 32):
+            base = stage_base(D, s, vb)
+            assert 0 <= base and base + 4096 <= TB
+            for a in range(4):
+                for lane in range(64):
+                    off, r, c0 = acc_write(lane, a)
+                    for e in range(4):
+                        lds[(base + off) // 4 + e] = tag(32 * s + r, vb * 32 + c0 + e)
+            for j in range(4):
+                for lane in range(64):
+                    off, R, c0 = row_read(lane, j)
+                    for e in range(4):
+                        out[32 * s + R, vb * 32 + c0 + e] = lds[(base + off) // 4 + e]
+    expect = np.array([[tag(r, c) for c in range(D)] for r in range(64)])
+    assert np.array_equal(out, expect)
+
+
+def test_epilogue_staging_is_free_of_bank_conflicts():
+    """A 16-byte LDS access of 16 lanes covers 256 bytes, all 64 banks, when the lanes' 16-byte
+    slots (address / 16 mod 16) are distinct; both access patterns meet that."""
+    for a in range(4):
+        for g in range(4):
+            assert len({(acc_write(l, a)[0] // 16) % 16 for l in range(16 * g, 16 * g + 16)}) == 16
+    for j in range(4):
+        for g in range(4):
+            assert len({(row_read(l, j)[0] // 16) % 16 for l in range(16 * g, 16 * g + 16)}) == 16
+
+
+@pytest.mark.parametrize("kt_live", [1, 2, 3, 7, 64])
+def test_every_copy_lands_before_the_epilogue(kt_live):
+    """The staging phase comes after the barrier that follows the loop's final vmcnt(0): no copy,
+    including the two past the last live tile, can still write a tile buffer there."""
+    copies, _ = events(kt_live, 3, 2, 4, 4)
+    assert max(last for _, _, _, last in copies) <= kt_live
