@@ -22,7 +22,11 @@
 // buffer_load ... lds; one XOR swizzle per tile keeps both the 16-byte operand reads and the
 // transposing reads free of bank conflicts.  Each output has one owner: no atomics.  Only
 // tiles holding an allowed pair are visited, and the element mask runs only on tiles that
-// cross the causal diagonal.
+// cross the causal diagonal.  dS is rounded to bf16 without the softmax scale (the same
+// relative precision), which dQ and dK take once, as they are written.  The dQ kernel issues
+// its dQ products at raised wave priority: of the two waves on a SIMD, the one with products
+// to issue goes first while the other forms its probabilities (in the key-stationary kernel
+// the same measured no gain).
 
 #include <hip/hip_runtime.h>
 
@@ -75,6 +79,13 @@ using ic = std::integral_constant<int, N>;
 // tile (k_roff: row r32, chunk 2*ks + hi) and where its transposing reads go (t_roff: rows
 // 4*(g>>1) + e (+8 for the second half, +16*kk as an immediate), columns 32*vb + 16*(g&1) +
 // 4*a), and which global chunk it fetches for each direct load.
+// x, through an empty asm statement the compiler cannot see into: what is computed from the
+// result starts here, not earlier
+__device__ __forceinline__ int opaque_copy(int x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
 template <int D, int BT>
 struct TileMap {
   static constexpr int KS = D / 16, VB = D / 32, RB = D * 2, CPR = D / 8, RPL = 64 / CPR;
@@ -221,19 +232,26 @@ void bwd_dq_kernel(BwdParams p) {
         s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(map.rd(kt_b, ks, kh), qf[ks], s, 0, 0, 0);
         dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(map.rd(vt_b, ks, kh), dof[ks], dp, 0, 0, 0);
       }
-      // lane holds keys 32*kh + 8*(j/4) + 4*hi + (j%4) of this row
+      // lane holds keys 32*kh + 8*(j/4) + 4*hi + (j%4) of this row.  dS is left unscaled here
+      // (bf16 keeps the same relative precision either way); dQ takes the softmax scale once,
+      // at the end.
+#pragma unroll
+      for (int j = 0; j < 16; ++j) s[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[j], c2, -lse2));
+      if (!full) {
+#pragma unroll
+        for (int j = 0; j < 16; ++j)
+          if (32 * kh + 8 * (j >> 2) + (j & 3) > lim) s[j] = 0.f;
+      }
       bf16x8 dsk[2];
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const bool ok = full || 32 * kh + 8 * (j >> 2) + (j & 3) <= lim;
-        const float pr = ok ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[j], c2, -lse2)) : 0.f;
-        dsk[j >> 3][j & 7] = (__bf16)(pr * (dp[j] - Dr) * p.scale);
-      }
+      for (int j = 0; j < 16; ++j) dsk[j >> 3][j & 7] = (__bf16)(s[j] * (dp[j] - Dr));
+      __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int k2 = 0; k2 < 2; ++k2)
 #pragma unroll
         for (int vb = 0; vb < VB; ++vb)
           dq[vb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(map.rd_t(kt_b, 2 * kh + k2, vb), dsk[k2], dq[vb], 0, 0, 0);
+      __builtin_amdgcn_s_setprio(0);
     }
     __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's copies of the next tile
     __syncthreads();
@@ -256,10 +274,10 @@ void bwd_dq_kernel(BwdParams p) {
       for (int a = 0; a < 4; ++a) {
         float4* q4 = reinterpret_cast<float4*>(op + vb * 32 + 8 * a);
         float4 x = *q4;
-        x.x += dq[vb][4 * a + 0];
-        x.y += dq[vb][4 * a + 1];
-        x.z += dq[vb][4 * a + 2];
-        x.w += dq[vb][4 * a + 3];
+        x.x += dq[vb][4 * a + 0] * p.scale;
+        x.y += dq[vb][4 * a + 1] * p.scale;
+        x.z += dq[vb][4 * a + 2] * p.scale;
+        x.w += dq[vb][4 * a + 3] * p.scale;
         *q4 = x;
       }
   }
@@ -389,7 +407,17 @@ void bwd_kv_kernel(BwdParams p) {
     const bool full = t0 + wave * KW + KW - 1 <= r0 + p.diag;
     const float4* lse4 = reinterpret_cast<const float4*>(&lse_t[B][0]);
     const float4* d4 = reinterpret_cast<const float4*>(&d_t[B][0]);
-    bf16x8 wp[2 * NH], ws[2 * NH];   // P and dS in bf16, per 16-row step
+    // Rows past the launch carry lse = +inf (p = 0) and keys past the block only feed their
+    // own, unstored, column: only tiles on the causal diagonal need the element mask, which
+    // sends a score to -inf (p = 0).
+    if (!full) {
+#pragma unroll
+      for (int rh = 0; rh < NH; ++rh)
+#pragma unroll
+        for (int j = 0; j < 16; ++j)
+          if (key > r0 + 32 * rh + 8 * (j >> 2) + 4 * hi + (j & 3) + p.diag) s[rh][j] = -INFINITY;
+    }
+    bf16x8 wp[2 * NH], ws[2 * NH];   // P and dS in bf16, per 16-row step; dS unscaled
 #pragma unroll
     for (int rh = 0; rh < NH; ++rh)
 #pragma unroll
@@ -401,12 +429,8 @@ void bwd_kv_kernel(BwdParams p) {
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
           const int j = 4 * a + c;
-          const int i = r0 + 32 * rh + 8 * a + 4 * hi + c;
-          // rows past the launch carry lse = +inf (p = 0) and keys past the block only feed
-          // their own, unstored, column: only the causal diagonal needs the element mask
-          const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s[rh][j], c2, -lv[c]));
-          const float pr = (full || key <= i + p.diag) ? e : 0.f;
-          ws[2 * rh + (j >> 3)][j & 7] = (__bf16)(pr * (dp[rh][j] - dvv[c]) * p.scale);
+          const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[rh][j], c2, -lv[c]));
+          ws[2 * rh + (j >> 3)][j & 7] = (__bf16)(pr * (dp[rh][j] - dvv[c]));
           wp[2 * rh + (j >> 3)][j & 7] = (__bf16)pr;
         }
       }
@@ -430,25 +454,28 @@ void bwd_kv_kernel(BwdParams p) {
     if (u + 1 < n_it) step(ic<1>{}, u + 1);
   }
 
-  // dK and dV of the wave's keys, added to the travelling block's accumulators
-  if (key_ok) {
-    const int64_t kbase = (((int64_t)b * p.kv_heads + g) * p.dkv_rows + key) * D + 4 * hi;
-    auto add = [&](float* out, const f32x16* acc) {
+  // dK and dV of the wave's keys, added to the travelling block's accumulators.  The address
+  // comes from a copy of the lane index made here, so that it is not held through the loop.
+  const int el = opaque_copy(lane);
+  const int ekey = t0 + wave * KW + (el & 31);
+  if (ekey < p.n_k) {
+    const int64_t kbase = (((int64_t)b * p.kv_heads + g) * p.dkv_rows + ekey) * D + 4 * (el >> 5);
+    auto add = [&](float* out, const f32x16* acc, float f) {
 #pragma unroll
       for (int vb = 0; vb < VB; ++vb)
 #pragma unroll
         for (int a = 0; a < 4; ++a) {
           float4* o4 = reinterpret_cast<float4*>(out + kbase + vb * 32 + 8 * a);
           float4 x = *o4;
-          x.x += acc[vb][4 * a + 0];
-          x.y += acc[vb][4 * a + 1];
-          x.z += acc[vb][4 * a + 2];
-          x.w += acc[vb][4 * a + 3];
+          x.x += acc[vb][4 * a + 0] * f;
+          x.y += acc[vb][4 * a + 1] * f;
+          x.z += acc[vb][4 * a + 2] * f;
+          x.w += acc[vb][4 * a + 3] * f;
           *o4 = x;
         }
     };
-    add(p.dk, acck);
-    add(p.dv, accv);
+    add(p.dk, acck, p.scale);
+    add(p.dv, accv, 1.f);
   }
 }
 

@@ -491,7 +491,11 @@ void step_bf16_kernel(StepParams p) {
         l_run[s] = r;
       }
 
-      // O~^T += V^T P^T; the transposed value operand comes from two transposing reads
+      // O~^T += V^T P^T; the transposed value operand comes from two transposing reads.  The
+      // wave issues these products at raised priority: of the two waves on a SIMD, the one with
+      // value products to issue goes first, and the other's probabilities fill the matrix
+      // core's shadow, which pulls the two into alternating phases.
+      __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int vb = 0; vb < VB; ++vb) {
         const unsigned char* base = vt_base + vb * 2048 + kk * 16 * 64 + vb0;
@@ -505,6 +509,7 @@ void step_bf16_kernel(StepParams p) {
         for (int s = 0; s < 2; ++s)
           oacc[s][vb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pk[s], oacc[s][vb], 0, 0, 0);
       }
+      __builtin_amdgcn_s_setprio(0);
     }
   };
 
