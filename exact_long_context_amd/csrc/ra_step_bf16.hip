@@ -380,8 +380,9 @@ void step_bf16_kernel(StepParams p) {
 
   // One 32-key tile from buffer B: S^T = K Q^T for both sub-tiles (each K fragment feeds
   // both), the guard on the reference, then per 16-key half the probabilities and
-  // O~^T += V^T P^T (each V fragment feeds both sub-tiles).  Working in halves keeps only 16
-  // keys' probabilities in registers.
+  // O~^T += V^T P^T (each V fragment feeds both sub-tiles).  Working in halves keeps about one
+  // half's probabilities in registers at a time (the second half's are formed while the first
+  // half's products issue).
   auto tile = [&](auto bufc, int kt) {
     const unsigned char* kt_base = ktile(bufc);
     const unsigned char* vt_base = vtile(bufc);
@@ -470,13 +471,11 @@ void step_bf16_kernel(StepParams p) {
       }
     }
 
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      // probabilities 2^(x - m_run) of keys 16kk .. 16kk+15, rounded to bf16: the B operand
-      // of the value product; this lane's share of the row sum adds the same rounded values
-      // (v_dot2 with ones), so the weights used for O~ and for l agree exactly and a row with
-      // a single visible key normalises to exactly 1
-      bf16x8 pk[2];
+    // Per 16-key half kk: the probabilities 2^(x - m_run) of keys 16kk .. 16kk+15, rounded to
+    // bf16, are the B operand of the value product; this lane's share of the row sum adds the
+    // same rounded values (v_dot2 with ones), so the weights used for O~ and for l agree exactly
+    // and a row with a single visible key normalises to exactly 1.
+    auto probs = [&](int kk, bf16x8* pk) {
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
 #pragma unroll
@@ -490,12 +489,10 @@ void step_bf16_kernel(StepParams p) {
         r = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pk[s], pk[s], 6, 7), ones, r, false);
         l_run[s] = r;
       }
-
-      // O~^T += V^T P^T; the transposed value operand comes from two transposing reads.  The
-      // wave issues these products at raised priority: of the two waves on a SIMD, the one with
-      // value products to issue goes first, and the other's probabilities fill the matrix
-      // core's shadow, which pulls the two into alternating phases.
-      __builtin_amdgcn_s_setprio(1);
+    };
+    // O~^T += V^T P^T for half kk; the transposed value operand comes from two transposing
+    // reads.
+    auto values = [&](int kk, const bf16x8* pk) {
 #pragma unroll
       for (int vb = 0; vb < VB; ++vb) {
         const unsigned char* base = vt_base + vb * 2048 + kk * 16 * 64 + vb0;
@@ -509,8 +506,19 @@ void step_bf16_kernel(StepParams p) {
         for (int s = 0; s < 2; ++s)
           oacc[s][vb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pk[s], oacc[s][vb], 0, 0, 0);
       }
-      __builtin_amdgcn_s_setprio(0);
-    }
+    };
+    // The wave raises its priority once the first half's probabilities are formed and keeps it
+    // through both halves' value products and the second half's probabilities.  Of the two waves
+    // on a SIMD, the one in this stretch goes first and the other's softmax fills the matrix
+    // core's shadow, which pulls the two into alternating phases; the second half's
+    // probabilities, at raised priority, issue between the first half's products.
+    bf16x8 pk0[2], pk1[2];
+    probs(0, pk0);
+    __builtin_amdgcn_s_setprio(1);
+    values(0, pk0);
+    probs(1, pk1);
+    values(1, pk1);
+    __builtin_amdgcn_s_setprio(0);
   };
 
   // One pipeline step for tile kt in buffer B = kt % 3: start the direct loads of tile kt+2
