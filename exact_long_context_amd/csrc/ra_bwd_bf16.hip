@@ -360,6 +360,7 @@ void bwd_kv_kernel(BwdParams p) {
     }
 
   // iteration u: head g*group + u / n_rt, query rows r_start + (u % n_rt) * BT ..
+  // The tile copies (the next tile past the last: a clamped head, never computed).
   auto stage = [&](int buf, int u) {
     const int hh = u / n_rt;
     const int r0 = r_start + (u % n_rt) * BT;
@@ -368,20 +369,33 @@ void bwd_kv_kernel(BwdParams p) {
     const __bf16* ob = static_cast<const __bf16*>(p.d_out) + (int64_t)b * p.q_sb + (int64_t)h * p.q_sh;
     map.load(q_tiles[buf], qb, r0, p.n_q, p.q_st, wave, row_bytes);
     map.load(o_tiles[buf], ob, r0, p.n_q, p.q_st, wave, row_bytes);
-    if (tid < BT) {
-      const int i = r0 + tid;
-      const bool ok = hh < p.group && i < p.n_q;
-      const int64_t sr = ((int64_t)b * p.q_heads + h) * p.state_rows + i;
-      // +inf for a row outside the launch or one that saw no key in the forward: 2^(x - lse) = 0
-      const float l2 = ok ? p.lse[sr] * kLog2e : INFINITY;
-      lse_t[buf][tid] = l2 == -INFINITY ? INFINITY : l2;
-      d_t[buf][tid] = ok ? p.D[sr] : 0.f;
-    }
+  };
+  // The tile's lse and D rows (the first BT lanes of wave 0) go through registers: loaded
+  // before the tile's copies are issued, written to LDS at the end of the step.  Loads complete
+  // in order, so a wait for them that followed the copies would wait for the whole tile; the
+  // loads are unconditional (a row past the launch reads nothing and returns 0), so that no
+  // branch joins their results before the end of the step.
+  auto fetch_rows = [&](int u, float& l, float& dd) {
+    const int hh = u / n_rt;
+    const int r0 = r_start + (u % n_rt) * BT;
+    const int64_t row0 = ((int64_t)b * p.q_heads + g * p.group + min(hh, p.group - 1)) * p.state_rows + r0;
+    const int64_t bytes = hh < p.group ? (int64_t)min(BT, p.n_q - r0) * 4 : 0;
+    l = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rsrc_bwd(p.lse + row0, bytes), tid * 4, 0, 0));
+    dd = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rsrc_bwd(p.D + row0, bytes), tid * 4, 0, 0));
+  };
+  auto put_rows = [&](int buf, int u, float l, float dd) {
+    const bool ok = u / n_rt < p.group && r_start + (u % n_rt) * BT + tid < p.n_q;
+    // +inf for a row outside the launch or one that saw no key in the forward: 2^(x - lse) = 0
+    const float l2 = l * kLog2e;
+    lse_t[buf][tid] = (!ok || l2 == -INFINITY) ? INFINITY : l2;
+    d_t[buf][tid] = dd;   // 0 past the launch's rows
   };
 
   auto step = [&](auto bufc, int u) {
     constexpr int B = decltype(bufc)::value;
-    stage(1 - B, u + 1);   // the next tile (past the last: a clamped head, rows masked out)
+    float nl, nd;
+    fetch_rows(u + 1, nl, nd);
+    stage(1 - B, u + 1);
     const int r0 = r_start + (u % n_rt) * BT;
     const unsigned char* qt_b = q_tiles[B];
     const unsigned char* ot_b = o_tiles[B];
@@ -442,11 +456,17 @@ void bwd_kv_kernel(BwdParams p) {
         accv[vb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(map.rd_t(ot_b, kk, vb), wp[kk], accv[vb], 0, 0, 0);
         acck[vb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(map.rd_t(qt_b, kk, vb), ws[kk], acck[vb], 0, 0, 0);
       }
+    if (tid < BT) put_rows(1 - B, u + 1, nl, nd);
     __builtin_amdgcn_s_waitcnt(0x0F70);
     __syncthreads();
   };
 
-  stage(0, 0);
+  {
+    float l0, d0;
+    fetch_rows(0, l0, d0);
+    stage(0, 0);
+    if (tid < BT) put_rows(0, 0, l0, d0);
+  }
   __builtin_amdgcn_s_waitcnt(0x0F70);
   __syncthreads();
   for (int u = 0; u < n_it; u += 2) {
