@@ -23,10 +23,9 @@
 // transposing reads free of bank conflicts.  Each output has one owner: no atomics.  Only
 // tiles holding an allowed pair are visited, and the element mask runs only on tiles that
 // cross the causal diagonal.  dS is rounded to bf16 without the softmax scale (the same
-// relative precision), which dQ and dK take once, as they are written.  The dQ kernel issues
-// its dQ products at raised wave priority: of the two waves on a SIMD, the one with products
-// to issue goes first while the other forms its probabilities (in the key-stationary kernel
-// the same measured no gain).
+// relative precision), which dQ and dK take once, as they are written.  Both kernels issue
+// their gradient products (dQ; dV and dK) at raised wave priority: of the two waves on a SIMD,
+// the one with products to issue goes first while the other forms its probabilities.
 
 #include <hip/hip_runtime.h>
 
@@ -220,39 +219,46 @@ void bwd_dq_kernel(BwdParams p) {
     // the wave
     const bool full = (kt + 1) * BT - 1 <= i0 + wave * WR + p.diag && (kt + 1) * BT <= p.n_k;
     const int lim = min(row + p.diag, p.n_k - 1) - kt * BT - 4 * hi;
-    // one 32-key half at a time (scores, dP, dS, then its share of dQ): with both halves' scores
-    // live at once this kernel spilled at d = 128
+    // The scores and dP of both 32-key halves first (four independent MFMA chains), then per
+    // half the probabilities, dS and that half's share of dQ, so that the second half's softmax
+    // can issue under the first half's dQ products.  From the first half's dQ products to the
+    // end of the tile the wave runs at raised priority: of the two waves on a SIMD, the one with
+    // products to issue goes first while the other forms its probabilities.
+    f32x16 s[NH], dp[NH];
+#pragma unroll
+    for (int kh = 0; kh < NH; ++kh)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) s[kh][j] = dp[kh][j] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int kh = 0; kh < NH; ++kh) {
+        s[kh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(map.rd(kt_b, ks, kh), qf[ks], s[kh], 0, 0, 0);
+        dp[kh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(map.rd(vt_b, ks, kh), dof[ks], dp[kh], 0, 0, 0);
+      }
+    // lane holds keys 32*kh + 8*(j/4) + 4*hi + (j%4) of this row.  dS is left unscaled here
+    // (bf16 keeps the same relative precision either way); dQ takes the softmax scale once, at
+    // the end.
 #pragma unroll
     for (int kh = 0; kh < NH; ++kh) {
-      f32x16 s, dp;
 #pragma unroll
-      for (int j = 0; j < 16; ++j) s[j] = dp[j] = 0.f;
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(map.rd(kt_b, ks, kh), qf[ks], s, 0, 0, 0);
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(map.rd(vt_b, ks, kh), dof[ks], dp, 0, 0, 0);
-      }
-      // lane holds keys 32*kh + 8*(j/4) + 4*hi + (j%4) of this row.  dS is left unscaled here
-      // (bf16 keeps the same relative precision either way); dQ takes the softmax scale once,
-      // at the end.
-#pragma unroll
-      for (int j = 0; j < 16; ++j) s[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[j], c2, -lse2));
+      for (int j = 0; j < 16; ++j) s[kh][j] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kh][j], c2, -lse2));
       if (!full) {
 #pragma unroll
         for (int j = 0; j < 16; ++j)
-          if (32 * kh + 8 * (j >> 2) + (j & 3) > lim) s[j] = 0.f;
+          if (32 * kh + 8 * (j >> 2) + (j & 3) > lim) s[kh][j] = 0.f;
       }
       bf16x8 dsk[2];
 #pragma unroll
-      for (int j = 0; j < 16; ++j) dsk[j >> 3][j & 7] = (__bf16)(s[j] * (dp[j] - Dr));
+      for (int j = 0; j < 16; ++j) dsk[j >> 3][j & 7] = (__bf16)(s[kh][j] * (dp[kh][j] - Dr));
       __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int k2 = 0; k2 < 2; ++k2)
 #pragma unroll
         for (int vb = 0; vb < VB; ++vb)
           dq[vb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(map.rd_t(kt_b, 2 * kh + k2, vb), dsk[k2], dq[vb], 0, 0, 0);
-      __builtin_amdgcn_s_setprio(0);
     }
+    __builtin_amdgcn_s_setprio(0);
     __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's copies of the next tile
     __syncthreads();
   };
@@ -448,7 +454,8 @@ void bwd_kv_kernel(BwdParams p) {
           wp[2 * rh + (j >> 3)][j & 7] = (__bf16)pr;
         }
       }
-    // dV^T += dO^T P; dK^T += Q^T dS
+    // dV^T += dO^T P; dK^T += Q^T dS, at raised wave priority (as in the dQ kernel)
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int kk = 0; kk < 2 * NH; ++kk)
 #pragma unroll
@@ -456,6 +463,7 @@ void bwd_kv_kernel(BwdParams p) {
         accv[vb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(map.rd_t(ot_b, kk, vb), wp[kk], accv[vb], 0, 0, 0);
         acck[vb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(map.rd_t(qt_b, kk, vb), ws[kk], acck[vb], 0, 0, 0);
       }
+    __builtin_amdgcn_s_setprio(0);
     if (tid < BT) put_rows(1 - B, u + 1, nl, nd);
     __builtin_amdgcn_s_waitcnt(0x0F70);
     __syncthreads();
