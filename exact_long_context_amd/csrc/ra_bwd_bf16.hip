@@ -438,10 +438,10 @@ void bwd_kv_kernel(BwdParams p) {
           if (key > r0 + 32 * rh + 8 * (j >> 2) + 4 * hi + (j & 3) + p.diag) s[rh][j] = -INFINITY;
     }
     bf16x8 wp[2 * NH], ws[2 * NH];   // P and dS in bf16, per 16-row step; dS unscaled
+    auto probs = [&](int kk) {   // rows 16kk .. 16kk+15 of the tile
+      const int rh = kk >> 1;
 #pragma unroll
-    for (int rh = 0; rh < NH; ++rh)
-#pragma unroll
-      for (int a = 0; a < 4; ++a) {
+      for (int a = 2 * (kk & 1); a < 2 * (kk & 1) + 2; ++a) {
         const float4 l4 = lse4[8 * rh + 2 * a + hi];   // rows 32rh + 8a + 4hi .. +3
         const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
         const float4 dd = d4[8 * rh + 2 * a + hi];
@@ -450,19 +450,28 @@ void bwd_kv_kernel(BwdParams p) {
         for (int c = 0; c < 4; ++c) {
           const int j = 4 * a + c;
           const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[rh][j], c2, -lv[c]));
-          ws[2 * rh + (j >> 3)][j & 7] = (__bf16)(pr * (dp[rh][j] - dvv[c]));
-          wp[2 * rh + (j >> 3)][j & 7] = (__bf16)pr;
+          ws[kk][j & 7] = (__bf16)(pr * (dp[rh][j] - dvv[c]));
+          wp[kk][j & 7] = (__bf16)pr;
         }
       }
-    // dV^T += dO^T P; dK^T += Q^T dS, at raised wave priority (as in the dQ kernel)
-    __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-    for (int kk = 0; kk < 2 * NH; ++kk)
+    };
+    auto grads = [&](int kk) {   // dV^T += dO^T P; dK^T += Q^T dS for those rows
 #pragma unroll
       for (int vb = 0; vb < VB; ++vb) {
         accv[vb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(map.rd_t(ot_b, kk, vb), wp[kk], accv[vb], 0, 0, 0);
         acck[vb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(map.rd_t(qt_b, kk, vb), ws[kk], acck[vb], 0, 0, 0);
       }
+    };
+    // The first 16 rows' P and dS, then at raised wave priority each 16 rows' products with the
+    // next 16 rows' P and dS formed between them: of the two waves on a SIMD, the one with
+    // products to issue goes first, and this wave's softmax issues under its own products.
+    probs(0);
+    __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+    for (int kk = 0; kk < 2 * NH; ++kk) {
+      grads(kk);
+      if (kk + 1 < 2 * NH) probs(kk + 1);
+    }
     __builtin_amdgcn_s_setprio(0);
     if (tid < BT) put_rows(1 - B, u + 1, nl, nd);
     __builtin_amdgcn_s_waitcnt(0x0F70);
