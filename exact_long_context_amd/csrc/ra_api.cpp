@@ -155,6 +155,30 @@ int64_t pairs_of(int32_t rows, int32_t keys, int32_t diag) {
   return n;
 }
 
+// Two sub-blocks of the same rows, b's keys right after a's, as one causal sub-block: possible
+// when every row sees a prefix of the joined keys (b's keys only where all of a's are visible)
+// and one diagonal gives every row's count.
+bool merge_keys(const Sub& a, const Sub& b, Sub* m) {
+  if (a.row0 != b.row0 || a.rows != b.rows || b.key0 != a.key0 + a.keys) return false;
+  const int32_t diag = b.diag + a.keys;
+  for (int32_t i = 0; i < a.rows; ++i) {
+    const int32_t na = ra::keys_visible(i, a.diag, a.keys), nb = ra::keys_visible(i, b.diag, b.keys);
+    if ((nb > 0 && na != a.keys) || ra::keys_visible(i, diag, a.keys + b.keys) != na + nb) return false;
+  }
+  *m = Sub{a.row0, a.rows, a.key0, a.keys + b.keys, diag, a.pairs + b.pairs};
+  return true;
+}
+
+// Two sub-blocks of the same keys, b's rows right after a's, as one: possible when a's
+// diagonal, continued over b's rows, gives every one of them its own count.
+bool merge_rows(const Sub& a, const Sub& b, Sub* m) {
+  if (a.key0 != b.key0 || a.keys != b.keys || b.row0 != a.row0 + a.rows) return false;
+  for (int32_t i = 0; i < b.rows; ++i)
+    if (ra::keys_visible(a.rows + i, a.diag, a.keys) != ra::keys_visible(i, b.diag, b.keys)) return false;
+  *m = Sub{a.row0, a.rows + b.rows, a.key0, a.keys, a.diag, a.pairs + b.pairs};
+  return true;
+}
+
 int subs_of(const ra_desc* d, int32_t kv_len, int32_t mask_kind, int64_t q_off, int64_t k_off,
             Sub* out, int* n_out) {
   if (kv_len < 0) return fail(RA_E_INVALID, "kv_len must be >= 0");
@@ -494,26 +518,55 @@ int ra_block_step(ra_state* st, const void* k, const void* v, int32_t kv_len, in
     if (e != hipSuccess) return hip_fail(e, "step kernel launch");
     return RA_OK;
   };
-  // Sub-blocks that share query rows run in order on the stream.  Only the first launch
-  // that touches a row range of a fresh state starts from the empty state; a fresh row
-  // range with no allowed pair in this block still gets the empty state written (with no
-  // keys), because the state stops being fresh as a whole.
-  const int per_rows = n_subs == 4 ? 2 : 1;
-  for (int g = 0; g < n_subs; g += per_rows) {
-    bool launched = false;
-    for (int u = g; u < g + per_rows; ++u) {
-      if (subs[u].pairs == 0) continue;
-      rc = launch(subs[u], st->fresh && !launched);
-      if (rc) return rc;
-      launched = true;
+  // The launches: the sub-blocks with an allowed pair, in order (those that share query rows
+  // run one after the other on the stream).  Zigzag chunk pairs that together form one causal
+  // sub-block exactly (the two key chunks of one query chunk, or both query chunks against one
+  // key chunk) run as one launch, which spares a launch's start and drain; only when the chunks
+  // are whole tiles, so that every tile, and every count the kernels keep, is the one the
+  // chunk pairs give.  covers[u]: the query chunks (bit per chunk) that launch u touches.
+  const bool zz = n_subs == 4;
+  Sub runs[4];
+  unsigned covers[4];
+  int n_runs = 0;
+  for (int u = 0; u < n_subs; ++u)
+    if (subs[u].pairs > 0) {
+      runs[n_runs] = subs[u];
+      covers[n_runs++] = zz ? 1u << (u >> 1) : 1u;
     }
-    if (!launched && st->fresh) {
-      Sub empty = subs[g];
-      empty.keys = 0;
-      rc = launch(empty, 1);
-      if (rc) return rc;
+  if (zz && subs[0].rows % tile_q_of(d) == 0 && subs[0].keys % tile_k_of(d) == 0) {
+    Sub m;
+    for (int a = 0; a + 1 < n_runs; ++a)
+      if (covers[a] == covers[a + 1] && merge_keys(runs[a], runs[a + 1], &m)) {
+        runs[a] = m;
+        for (int u = a + 1; u + 1 < n_runs; ++u) {
+          runs[u] = runs[u + 1];
+          covers[u] = covers[u + 1];
+        }
+        --n_runs;
+      }
+    if (n_runs == 2 && covers[0] != covers[1] && merge_rows(runs[0], runs[1], &m)) {
+      runs[0] = m;
+      covers[0] |= covers[1];
+      n_runs = 1;
     }
   }
+  // Only the first launch that touches a row range of a fresh state starts from the empty
+  // state; a fresh row range with no allowed pair in this block still gets the empty state
+  // written (with no keys), because the state stops being fresh as a whole.
+  unsigned touched = 0;
+  for (int u = 0; u < n_runs; ++u) {
+    rc = launch(runs[u], st->fresh && (covers[u] & touched) == 0);
+    if (rc) return rc;
+    touched |= covers[u];
+  }
+  if (st->fresh)
+    for (int c = 0; c < (zz ? 2 : 1); ++c)
+      if (!((touched >> c) & 1u)) {
+        Sub empty = subs[zz ? 2 * c : 0];
+        empty.keys = 0;
+        rc = launch(empty, 1);
+        if (rc) return rc;
+      }
   st->fresh = 0;
   add_stats(&st->stats, &s);
   return RA_OK;
