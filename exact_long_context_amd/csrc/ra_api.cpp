@@ -430,8 +430,24 @@ int ra_state_resume(const ra_desc* desc, const void* q, void* workspace, ra_stat
   return make_state(desc, q, workspace, 0, out);
 }
 
+namespace {
+int block_step(ra_state* st, const void* k, const void* v, int32_t kv_len, int32_t mask_kind,
+               int64_t q_offset, int64_t k_offset, float* fin_o, float* fin_lse, int* finalized);
+}  // namespace
+
 int ra_block_step(ra_state* st, const void* k, const void* v, int32_t kv_len, int32_t mask_kind,
                   int64_t q_offset, int64_t k_offset) {
+  return block_step(st, k, v, kv_len, mask_kind, q_offset, k_offset, nullptr, nullptr, nullptr);
+}
+
+namespace {
+// fin_o (optional): the block is the lap's last, and O and lse are wanted; when the step runs
+// as one bf16 launch over all rows in which every row sees a key, that launch writes O = O~ / l
+// and lse as it writes back (the arithmetic of the finalize pass), the state is finalized and
+// *finalized is 1.  Otherwise the step keeps the state as usual and *finalized is 0.
+int block_step(ra_state* st, const void* k, const void* v, int32_t kv_len, int32_t mask_kind,
+               int64_t q_offset, int64_t k_offset, float* fin_o, float* fin_lse, int* finalized) {
+  if (finalized) *finalized = 0;
   if (!st) return fail(RA_E_INVALID, "state is NULL");
   if (st->finalized) return fail(RA_E_STATE, "step after finalize");
   const ra_desc* d = &st->desc;
@@ -485,6 +501,7 @@ int ra_block_step(ra_state* st, const void* k, const void* v, int32_t kv_len, in
       knorm = st->knorm;
     }
   }
+  bool fin = false;   // set once the launches are known
   auto launch = [&](const Sub& b, int fresh) -> int {
     ra::StepParams p;
     p.q = static_cast<const char*>(st->q) + (int64_t)b.row0 * d->q_strides[2] * elem;
@@ -513,6 +530,14 @@ int ra_block_step(ra_state* st, const void* k, const void* v, int32_t kv_len, in
     // tiles of a sub-block line up with the block's when it starts on a tile boundary
     p.knorm = knorm && b.key0 % ra::kBf16TileK == 0 ? knorm + b.key0 / ra::kBf16TileK : nullptr;
     p.knorm_stride = n_tiles;
+    p.o_out = p.o_acc;
+    p.fin_lse = nullptr;
+    p.finalize = 0;
+    if (fin) {
+      p.o_out = fin_o + (int64_t)b.row0 * d->head_dim;
+      p.fin_lse = fin_lse ? fin_lse + b.row0 : nullptr;
+      p.finalize = 1;
+    }
     hipError_t e = d->dtype == RA_DTYPE_BF16 ? ra::launch_step_bf16(p, d->head_dim, stream)
                                              : ra::launch_step_f32(p, d->head_dim, stream);
     if (e != hipSuccess) return hip_fail(e, "step kernel launch");
@@ -550,6 +575,10 @@ int ra_block_step(ra_state* st, const void* k, const void* v, int32_t kv_len, in
       n_runs = 1;
     }
   }
+  // The lap's last step finalizes in its launch when that launch is the whole step, covers
+  // every row and every row sees a key (no workgroup then returns early).
+  fin = fin_o && d->dtype == RA_DTYPE_BF16 && n_runs == 1 && runs[0].row0 == 0 && runs[0].rows == d->q_len &&
+        ra::keys_visible(0, runs[0].diag, runs[0].keys) > 0 && aligned16(fin_o);
   // Only the first launch that touches a row range of a fresh state starts from the empty
   // state; a fresh row range with no allowed pair in this block still gets the empty state
   // written (with no keys), because the state stops being fresh as a whole.
@@ -569,8 +598,13 @@ int ra_block_step(ra_state* st, const void* k, const void* v, int32_t kv_len, in
       }
   st->fresh = 0;
   add_stats(&st->stats, &s);
+  if (fin) {
+    st->finalized = 1;
+    if (finalized) *finalized = 1;
+  }
   return RA_OK;
 }
+}  // namespace
 
 int ra_finalize(ra_state* st, float* o, float* lse) {
   if (!st) return fail(RA_E_INVALID, "state is NULL");
@@ -976,4 +1010,8 @@ int ra_version(void) { return 1; }
 namespace ra {
 int set_error(int code, const char* msg) { return fail(code, "%s", msg); }
 int set_hip_error(hipError_t e, const char* what) { return hip_fail(e, what); }
+int block_step_final(ra_state* st, const void* k, const void* v, int32_t kv_len, int32_t mask_kind,
+                     int64_t q_offset, int64_t k_offset, float* o, float* lse, int* finalized) {
+  return block_step(st, k, v, kv_len, mask_kind, q_offset, k_offset, o, lse, finalized);
+}
 }  // namespace ra

@@ -34,6 +34,13 @@ struct StepParams {
   // no bound, every tile takes the per-score guard
   const float* knorm;
   int32_t knorm_stride;
+  // Where the write-back goes: O~ (o_out = o_acc), or, when the lap's last step finalizes as
+  // it writes back (bf16 only; finalize = 1), O = O~ / l to o_out (laid out like O~) and lse to
+  // fin_lse (may be null) instead of O~, m and l to the state.  A finalizing launch must be one
+  // in which every row sees a key, so that no workgroup returns early.
+  float* o_out;
+  float* fin_lse;
+  int32_t finalize;
 };
 
 struct FinalizeParams {

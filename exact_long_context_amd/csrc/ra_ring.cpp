@@ -14,6 +14,10 @@
 //
 // Block visit order: at step s rank r holds block (r - s) mod P, the order of the
 // four-device table on the same page (section 环是怎样工作的).
+//
+// The last step finalizes as it writes back when one launch covers all of it and every row
+// sees a key (the output normalisation of "GPU ring attention", section "Why partial results
+// are allowed to merge", applied in the step kernel's write-back): one pass over the state less.
 
 #include <hip/hip_runtime.h>
 
@@ -25,6 +29,8 @@
 namespace ra {
 int set_error(int code, const char* msg);
 int set_hip_error(hipError_t e, const char* what);
+int block_step_final(ra_state* st, const void* k, const void* v, int32_t kv_len, int32_t mask_kind,
+                     int64_t q_offset, int64_t k_offset, float* o, float* lse, int* finalized);
 }  // namespace ra
 
 namespace {
@@ -92,6 +98,7 @@ extern "C" int ra_ring_lap_emulated(const ra_desc* desc, const void* q, void* wo
 
   const int r = lap->rank;
   const bool copies = lap->kv_len > 0 && P > 1;
+  int finalized = 0;
   // positions of step s's block, and whether any query of this rank sees a key of it
   auto offsets = [&](int j, int64_t* q_off, int64_t* k_off) {
     *q_off = 0;
@@ -149,7 +156,9 @@ extern "C" int ra_ring_lap_emulated(const ra_desc* desc, const void* q, void* wo
       return ra::set_hip_error(e, "event record");
     // padding past a block's real keys is cut off by the key count: no query sees it
     const int32_t keys = keys_of(j);
-    rc = ra_block_step(g.st, kp, vp, keys, lap->mask_kind, q_off, k_off);
+    // the last block may finalize as its launch writes back (then no separate finalize pass)
+    rc = s + 1 < P ? ra_block_step(g.st, kp, vp, keys, lap->mask_kind, q_off, k_off)
+                   : ra::block_step_final(g.st, kp, vp, keys, lap->mask_kind, q_off, k_off, o, lse, &finalized);
     if (rc) return rc;
     if (lap->step_events &&
         (e = hipEventRecord(static_cast<hipEvent_t>(lap->step_events[2 * s + 1]), cs)) != hipSuccess)
@@ -157,8 +166,7 @@ extern "C" int ra_ring_lap_emulated(const ra_desc* desc, const void* q, void* wo
     if (copies && s > 0 && (e = hipEventRecord(ev.freed[s & 1], cs)) != hipSuccess)
       return ra::set_hip_error(e, "event record");
   }
-  rc = ra_finalize(g.st, o, lse);
-  if (rc) return rc;
+  if (!finalized && (rc = ra_finalize(g.st, o, lse)) != RA_OK) return rc;
   if (stats_out) ra_get_stats(g.st, stats_out);
   return RA_OK;
 }

@@ -555,18 +555,26 @@ void step_bf16_kernel(StepParams p) {
   // computed before the loop and held through it
   const int el = opaque_copy(lane);
   const int e32 = el & 31, ehi = el >> 5;
+  // The lap's last step may finalize here instead (p.finalize): O = O~ / l and lse in place of
+  // O~, m and l, the arithmetic of the finalize pass.  A step that keeps the state scales by 1.
+  const bool fin = p.finalize != 0;
 #pragma unroll
   for (int s = 0; s < 2; ++s) {
     float la, lb;
     pair32(l_run[s], la, lb);
     const float l_row = la + lb;
     if (row_ok[s] && hi == 0) {
-      p.m[srow[s]] = l_row == 0.f ? -INFINITY : m_run[s];
-      p.l[srow[s]] = l_row;
+      if (!fin) {
+        p.m[srow[s]] = l_row == 0.f ? -INFINITY : m_run[s];
+        p.l[srow[s]] = l_row;
+      } else if (p.fin_lse) {
+        p.fin_lse[srow[s]] = l_row > 0.f ? 0.69314718055994530942f * (m_run[s] + log2f(l_row)) : -INFINITY;
+      }
     }
+    const float f = !fin ? 1.0f : l_row > 0.f ? 1.0f / l_row : 0.f;
     // the sub-tile's rows through a resource that ends at the last row: stores past it are dropped
     const __amdgpu_buffer_rsrc_t rs =
-        make_rsrc(p.o_acc + (((int64_t)b * p.q_heads + h) * p.state_rows + w0 + 32 * s) * D,
+        make_rsrc(p.o_out + (((int64_t)b * p.q_heads + h) * p.state_rows + w0 + 32 * s) * D,
                   (int64_t)max(0, p.n_q - w0 - 32 * s) * D * 4);
 #pragma unroll
     for (int vb = 0; vb < VB; ++vb) {
@@ -575,7 +583,8 @@ void step_bf16_kernel(StepParams p) {
 #pragma unroll
       for (int a = 0; a < 4; ++a)
         *reinterpret_cast<f32x4*>(half + e32 * 128 + (((2 * a + ehi) ^ ((e32 >> 1) & 7)) * 16)) =
-            f32x4{oacc[s][vb][4 * a + 0], oacc[s][vb][4 * a + 1], oacc[s][vb][4 * a + 2], oacc[s][vb][4 * a + 3]};
+            f32x4{oacc[s][vb][4 * a + 0] * f, oacc[s][vb][4 * a + 1] * f, oacc[s][vb][4 * a + 2] * f,
+                  oacc[s][vb][4 * a + 3] * f};
       f32x4 x[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
