@@ -413,14 +413,19 @@ void bwd_kv_kernel(BwdParams p) {
         s[rh][j] = 0.f;
         dp[rh][j] = 0.f;
       }
+    // the scores first, then dP: the exponentials need only the scores and can issue under the
+    // dP products
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int rh = 0; rh < NH; ++rh)
+        s[rh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(map.rd(qt_b, ks, rh), kf[ks], s[rh], 0, 0, 0);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       const bf16x8 vb8 = *(lds_cvbf16x8*)(v_park + (wave * KS + ks) * 1024 + lane * 16);
 #pragma unroll
-      for (int rh = 0; rh < NH; ++rh) {
-        s[rh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(map.rd(qt_b, ks, rh), kf[ks], s[rh], 0, 0, 0);
+      for (int rh = 0; rh < NH; ++rh)
         dp[rh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(map.rd(ot_b, ks, rh), vb8, dp[rh], 0, 0, 0);
-      }
     }
     // lane holds key `key` against tile rows 32*rh + 8*(j/4) + 4*hi + (j%4); a tile whose
     // first row sees the wave's last key needs no element mask
