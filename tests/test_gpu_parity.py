@@ -242,9 +242,10 @@ def test_order_invariance_and_state_resume_bitwise():
 
 @pytest.mark.parametrize("N", [4096, 32768], ids=["blocks512", "blocks4096"])
 def test_emulated_ring_lap_matches_steps_and_poison(N):
-    """The emulated lap equals the same blocks stepped one by one, bit for bit, with and
-    without poisoned receive buffers.  With blocks of 4096 keys the lap computes each received
-    block's key-norm bounds on its transfer stream, the steps inside ra_block_step."""
+    """The emulated lap equals the same blocks stepped one by one and then finalized, bit for
+    bit, with and without poisoned receive buffers.  The non-causal lap's last step finalizes in
+    its own write-back; the other layouts' last steps leave rows without a visible key (or skip
+    the block), so their laps run the separate finalize pass."""
     import exact_long_context_amd as ra
     P = 8
     # contiguous ranks 0 and 2 skip seven and five blocks: their receive buffers are freed on
