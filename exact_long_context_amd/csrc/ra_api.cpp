@@ -169,6 +169,16 @@ bool merge_keys(const Sub& a, const Sub& b, Sub* m) {
   return true;
 }
 
+// A sub-block with the empty sub-block beside it (same rows, b's keys right after a's) taken
+// in: possible when none of its rows sees b's keys under its own diagonal.
+bool extend_keys(const Sub& a, const Sub& b, Sub* m) {
+  if (a.row0 != b.row0 || a.rows != b.rows || b.key0 != a.key0 + a.keys || b.pairs != 0) return false;
+  for (int32_t i = 0; i < a.rows; ++i)
+    if (ra::keys_visible(i, a.diag, a.keys + b.keys) != ra::keys_visible(i, a.diag, a.keys)) return false;
+  *m = Sub{a.row0, a.rows, a.key0, a.keys + b.keys, a.diag, a.pairs};
+  return true;
+}
+
 // Two sub-blocks of the same keys, b's rows right after a's, as one: possible when a's
 // diagonal, continued over b's rows, gives every one of them its own count.
 bool merge_rows(const Sub& a, const Sub& b, Sub* m) {
@@ -569,7 +579,13 @@ int block_step(ra_state* st, const void* k, const void* v, int32_t kv_len, int32
         }
         --n_runs;
       }
-    if (n_runs == 2 && covers[0] != covers[1] && merge_rows(runs[0], runs[1], &m)) {
+    // both query chunks against one key chunk; or, on the rank's own block, the first query
+    // chunk's diagonal pair with its empty neighbour and the second chunk's joined pairs: one
+    // causal block over both chunks
+    Sub ext;
+    if (n_runs == 2 && covers[0] == 1u && covers[1] == 2u &&
+        (merge_rows(runs[0], runs[1], &m) ||
+         (extend_keys(runs[0], subs[1], &ext) && merge_rows(ext, runs[1], &m)))) {
       runs[0] = m;
       covers[0] |= covers[1];
       n_runs = 1;
